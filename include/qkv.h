@@ -1,0 +1,140 @@
+/*
+ * qkv.h -- C ABI of the fused attention-input library for AMD Instinct MI355X (gfx950).
+ *
+ * One call computes, for T tokens, the attention-input chain of a Llama-style
+ * decoder layer:
+ *
+ *     r[t]   = 1 / sqrt( (1/H) * sum_k x[t,k]^2 + eps )              (RMSNorm row reduction)
+ *     a[t,k] = x[t,k] * r[t] * w_norm[k]                             (normalised activations)
+ *     y[t,n] = sum_k a[t,k] * W[k,n]  (+ bias[n])                    (QKV projection)
+ *     Q, K   = rotate-half rotary embedding of the Q and K heads of y at position pos[t]
+ *     V      = the V heads of y, unrotated
+ *
+ * The chain is the one the page "Liger-Kernel底层优化：新一代内核级推理加速引擎介绍"
+ * (Liger-Kernel low-level optimisation: a new kernel-level inference acceleration
+ * engine) lists for one decoder layer in its opening section (rms_norm, proj_qkv,
+ * apply_rope on q and on k), and that the same page's section
+ * "融合内核是如何工作的？来看一段简化版实现" (how the fused kernel works) sketches as
+ * a single fused kernel: eps inside the reciprocal square root over the mean of
+ * squares, the weight multiplying each normalised element, the bias added before
+ * the rotation, and feature i of a head paired with feature i + head_dim/2.
+ * The rotation turns each pair (u, v) by +phi, phi = pos * theta^(-2i/head_dim):
+ *     (u, v) -> (u*cos(phi) - v*sin(phi), v*cos(phi) + u*sin(phi)).
+ *
+ * Layouts (all dense, row-major, no strides):
+ *     x      [T, H]                 dtype of the plan
+ *     w_norm [H]                    dtype of the plan
+ *     w_qkv  [H, N]                 dtype of the plan; N = (nq + 2*nkv) * head_dim;
+ *                                   columns = Q heads | K heads | V heads, each head's
+ *                                   head_dim columns contiguous
+ *     bias   [N] or NULL            dtype of the plan
+ *     pos    [T] int32              position id of each token (any int32 value)
+ *     q      [T, nq*head_dim]       written, dtype of the plan
+ *     k, v   [T, nkv*head_dim]      written, dtype of the plan
+ *
+ * Precision: bf16 plans take bf16 inputs and write bf16 outputs (round to nearest
+ * even); products accumulate in fp32.  fp32 plans compute in fp32 throughout.
+ *
+ * Ownership: the caller owns every tensor, allocates the outputs, and keeps all
+ * buffers alive until the work queued on `stream` has finished.  A plan owns only
+ * its device scratch (per-token inverse RMS values, decode partial sums and
+ * counters, the rotary frequency table), allocated on the device that is current
+ * when the plan is created and freed by qkv_plan_destroy.
+ *
+ * Errors: every call returns a status code; nothing is thrown across the ABI.
+ * Arguments are validated before any HIP call is made.
+ */
+#ifndef QKV_MI355X_H
+#define QKV_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qkv_status {
+  QKV_OK = 0,
+  QKV_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, malformed descriptor */
+  QKV_ERR_UNSUPPORTED = 2,   /* well-formed request outside what the kernels implement  */
+  QKV_ERR_HIP = 3,           /* a HIP runtime call or kernel launch failed              */
+  QKV_ERR_OUT_OF_MEMORY = 4  /* device scratch allocation failed                        */
+} qkv_status;
+
+typedef enum qkv_dtype {
+  QKV_F32 = 0,
+  QKV_BF16 = 1
+} qkv_dtype;
+
+/* Kernel path a forward of a given token count runs on (see qkv_plan_variant). */
+typedef enum qkv_variant {
+  QKV_VARIANT_GENERIC = 0,  /* fp32 FMA tiles: any supported shape, both dtypes        */
+  QKV_VARIANT_PREFILL = 1,  /* bf16 MFMA GEMM, norm-on-load, rotary epilogue           */
+  QKV_VARIANT_DECODE = 2    /* bf16 MFMA weight-streaming kernel for small token counts */
+} qkv_variant;
+
+typedef struct qkv_plan_s* qkv_plan;
+
+typedef struct qkv_plan_desc {
+  int64_t max_tokens;     /* upper bound on T for every forward through this plan (>= 1) */
+  int32_t hidden;         /* H: multiple of 8                                            */
+  int32_t num_q_heads;    /* nq >= 1                                                     */
+  int32_t num_kv_heads;   /* nkv >= 1, nq % nkv == 0 (MHA when equal, GQA otherwise)     */
+  int32_t head_dim;       /* even; the kernels implement multiples of 8                  */
+  int32_t dtype;          /* qkv_dtype                                                   */
+  int32_t has_bias;       /* 0 or 1                                                      */
+  double eps;             /* >= 0, finite; added to the mean square inside the sqrt      */
+  double rope_theta;      /* > 0, finite; rotary base                                    */
+} qkv_plan_desc;
+
+/* Validate `desc`, pick the kernel variants, allocate the plan's device scratch on
+ * the current device and return an opaque handle in *out_plan.
+ * Returns QKV_ERR_INVALID_ARG for a malformed descriptor or null pointers,
+ * QKV_ERR_UNSUPPORTED for shapes outside the kernels (head_dim not a multiple of 8,
+ * tensors whose byte size reaches 2^31), QKV_ERR_HIP when no device is usable and
+ * QKV_ERR_OUT_OF_MEMORY when the scratch cannot be allocated.  On error *out_plan is
+ * left NULL. */
+qkv_status qkv_plan_create(const qkv_plan_desc* desc, qkv_plan* out_plan);
+
+/* Queue one forward of T = num_tokens tokens on `stream` (a hipStream_t; NULL is the
+ * null stream).  Asynchronous: returns once the kernels are queued; allocates
+ * nothing and never synchronises the host.  T == 0 is a no-op that returns QKV_OK
+ * without touching any pointer.  For T >= 1: every pointer except `bias` must be
+ * non-null; `bias` must be non-null exactly when the plan has has_bias = 1; x,
+ * w_norm, w_qkv, bias, q, k and v must be 16-byte aligned and pos 4-byte aligned;
+ * 1 <= T <= max_tokens.  Violations return QKV_ERR_INVALID_ARG before anything is
+ * queued.  The device current at the call must be the plan's device.
+ * Forwards through the same plan share its scratch: two forwards through one plan
+ * on different streams may not overlap in time (use one plan per stream).
+ * Launch failures return QKV_ERR_HIP. */
+qkv_status qkv_forward(qkv_plan plan, int64_t num_tokens,
+                       const void* x, const void* w_norm, const void* w_qkv,
+                       const void* bias, const int32_t* pos,
+                       void* q, void* k, void* v, void* stream);
+
+/* Queue only the row reduction of the chain: inv_rms[t] = 1/sqrt(mean_k x[t,k]^2 + eps)
+ * as fp32 for t < num_tokens, into the caller's device buffer `inv_rms` (4-byte
+ * aligned).  Same argument rules, asynchrony and errors as qkv_forward. */
+qkv_status qkv_rms_inv(qkv_plan plan, int64_t num_tokens, const void* x,
+                       float* inv_rms, void* stream);
+
+/* Which variant a forward of num_tokens tokens runs on, in *variant (a qkv_variant).
+ * Host-only; returns QKV_ERR_INVALID_ARG for a bad plan or num_tokens out of range. */
+qkv_status qkv_plan_variant(qkv_plan plan, int64_t num_tokens, int32_t* variant);
+
+/* Release the plan's scratch and the handle.  NULL is a no-op returning QKV_OK.
+ * Waits for the plan's device to finish queued work before freeing.  A handle that
+ * was already destroyed is detected on a best-effort basis (QKV_ERR_INVALID_ARG). */
+qkv_status qkv_plan_destroy(qkv_plan plan);
+
+/* Static, NUL-terminated description of a status code ("unknown status" otherwise). */
+const char* qkv_status_string(qkv_status status);
+
+/* Static name of a variant ("generic", "prefill", "decode"; "unknown" otherwise). */
+const char* qkv_variant_name(int32_t variant);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKV_MI355X_H */

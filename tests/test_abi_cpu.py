@@ -1,0 +1,111 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/qkv.h declares, and rejects malformed arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_rmsnorm_row_amd as qkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qkv.h")
+
+
+def declared_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qkv_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("qkv_plan_create", "qkv_forward", "qkv_plan_destroy", "qkv_status_string"):
+        assert n in names
+    assert set(names) == set(qkv.EXPORTS), "binding and header disagree"
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qkv.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_status_and_variant_strings():
+    lib = qkv.load_library()
+    assert lib.qkv_status_string(0) == b"ok"
+    assert lib.qkv_status_string(1) == b"invalid argument"
+    assert lib.qkv_status_string(2).startswith(b"unsupported")
+    assert lib.qkv_status_string(99) == b"unknown status"
+    assert [lib.qkv_variant_name(i) for i in range(3)] == [b"generic", b"prefill", b"decode"]
+    assert lib.qkv_variant_name(7) == b"unknown"
+
+
+def _create(**over):
+    lib = qkv.load_library()
+    base = dict(max_tokens=16, hidden=64, num_q_heads=4, num_kv_heads=4, head_dim=16, dtype=0, has_bias=0,
+                eps=1e-6, rope_theta=1e4)
+    base.update(over)
+    d = qkv.PlanDesc(**base)
+    h = ctypes.c_void_p()
+    st = lib.qkv_plan_create(ctypes.byref(d), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(max_tokens=0), qkv.QKV_ERR_INVALID_ARG),
+    (dict(max_tokens=-5), qkv.QKV_ERR_INVALID_ARG),
+    (dict(hidden=0), qkv.QKV_ERR_INVALID_ARG),
+    (dict(num_q_heads=0), qkv.QKV_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), qkv.QKV_ERR_INVALID_ARG),
+    (dict(num_q_heads=6, num_kv_heads=4), qkv.QKV_ERR_INVALID_ARG),
+    (dict(head_dim=15), qkv.QKV_ERR_INVALID_ARG),
+    (dict(head_dim=0), qkv.QKV_ERR_INVALID_ARG),
+    (dict(dtype=2), qkv.QKV_ERR_INVALID_ARG),
+    (dict(has_bias=2), qkv.QKV_ERR_INVALID_ARG),
+    (dict(eps=-1.0), qkv.QKV_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), qkv.QKV_ERR_INVALID_ARG),
+    (dict(rope_theta=0.0), qkv.QKV_ERR_INVALID_ARG),
+    (dict(rope_theta=float("inf")), qkv.QKV_ERR_INVALID_ARG),
+    (dict(hidden=60), qkv.QKV_ERR_UNSUPPORTED),
+    (dict(head_dim=6), qkv.QKV_ERR_UNSUPPORTED),
+    (dict(max_tokens=1 << 40), qkv.QKV_ERR_UNSUPPORTED),
+    (dict(hidden=1 << 16, num_q_heads=64, num_kv_heads=64, head_dim=256, dtype=1), qkv.QKV_ERR_UNSUPPORTED),
+])
+def test_bad_descriptor_rejected_before_any_hip_call(over, expect):
+    st, h = _create(**over)
+    assert st == expect
+    assert h.value is None
+
+
+def test_null_pointers_rejected():
+    lib = qkv.load_library()
+    h = ctypes.c_void_p()
+    assert lib.qkv_plan_create(None, ctypes.byref(h)) == qkv.QKV_ERR_INVALID_ARG
+    d = qkv.PlanDesc(16, 64, 4, 4, 16, 0, 0, 1e-6, 1e4)
+    assert lib.qkv_plan_create(ctypes.byref(d), None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_forward(None, 4, *([None] * 8), None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_rms_inv(None, 4, None, None, None) == qkv.QKV_ERR_INVALID_ARG
+    v = ctypes.c_int32()
+    assert lib.qkv_plan_variant(None, 4, ctypes.byref(v)) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_plan_destroy(None) == qkv.QKV_OK
+
+
+def test_unknown_handle_rejected():
+    lib = qkv.load_library()
+    fake = ctypes.create_string_buffer(256)
+    assert lib.qkv_plan_destroy(ctypes.cast(fake, ctypes.c_void_p)) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_forward(ctypes.cast(fake, ctypes.c_void_p), 1, *([None] * 8), None) == qkv.QKV_ERR_INVALID_ARG
+
+
+def test_valid_descriptor_without_gpu():
+    """Without a device a valid descriptor gets past validation and fails at the first
+    HIP call; with one it yields a plan."""
+    lib = qkv.load_library()
+    st, h = _create()
+    if st == qkv.QKV_OK:
+        assert lib.qkv_plan_destroy(h) == qkv.QKV_OK
+        assert lib.qkv_plan_destroy(h) == qkv.QKV_ERR_INVALID_ARG
+    else:
+        assert st == qkv.QKV_ERR_HIP
+        assert h.value is None

@@ -1,0 +1,234 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI.
+
+Bar: |gpu - oracle| <= tol * (1 + |oracle|) elementwise on Q, K and V separately,
+tol = 1e-4 for the fp32 workload and 2e-2 for the bf16 ones; NaN or Inf fails.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_rmsnorm_row_amd as qkv
+import workloads
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def run(plan, inp, stream=None):
+    x = inp["x"].to(DEV)
+    w = inp["w_norm"].to(DEV)
+    W = inp["w_qkv"].to(DEV)
+    b = None if inp["bias"] is None else inp["bias"].to(DEV)
+    pos = inp["pos"].to(DEV)
+    out = plan.forward(x, w, W, b, pos, stream=stream)
+    torch.cuda.synchronize()
+    return out
+
+
+def shaped(wl, **kw):
+    return dataclasses.replace(wl, **kw)
+
+
+# ---------------------------------------------------------------- the five workloads
+
+def test_tiny_fp32_full():
+    wl = workloads.WORKLOADS[1]
+    inp = workloads.make_inputs(wl)
+    with qkv.Plan.for_workload(wl) as plan:
+        got = run(plan, inp)
+    ref = P.oracle_forward(wl, inp)
+    print(P.assert_parity(got, ref, P.TOL["fp32"], wl.name))
+
+
+def test_decode_full():
+    wl = workloads.WORKLOADS[4]
+    inp = workloads.make_inputs(wl)
+    with qkv.Plan.for_workload(wl) as plan:
+        got = run(plan, inp)
+    ref = P.oracle_forward(wl, inp)
+    print(P.assert_parity(got, ref, P.TOL["bf16"], wl.name))
+
+
+@pytest.mark.parametrize("cid", [2, 3, 5])
+def test_prefill_full_size_sampled_rows(cid):
+    """Full-size forward in the benchmark's launch configuration; the oracle evaluates
+    a sample of rows (ends, tile edges, random) one token at a time."""
+    wl = workloads.WORKLOADS[cid]
+    inp = workloads.make_inputs(wl)
+    with qkv.Plan.for_workload(wl) as plan:
+        got = run(plan, inp)
+    for t in got:
+        assert torch.isfinite(t).all(), "non-finite output"
+    rows = P.sample_rows(wl.tokens, 192, seed=cid)
+    ref = P.oracle_forward(wl, inp, rows=rows)
+    print(P.assert_parity(got, ref, P.TOL["bf16"], wl.name, rows=rows))
+
+
+# ---------------------------------------------------------------- ragged sizes, full comparison
+
+MEDIUM = [
+    (2, 1, 300),     # MHA 32x128, two full 128-row blocks + tail
+    (3, 1, 777),     # GQA 32/8, several 256-row tiles + ragged tail
+    (5, 1, 513),     # MHA with bias, one row past two tiles
+    (4, 1, 129),     # decode shape at a small prefill size
+]
+
+
+@pytest.mark.parametrize("cid,batch,seq", MEDIUM)
+def test_ragged_full_comparison(cid, batch, seq):
+    wl = workloads.WORKLOADS[cid].with_tokens(batch, seq)
+    inp = workloads.make_inputs(wl, seed=31 * cid + seq)
+    with qkv.Plan.for_workload(wl) as plan:
+        got = run(plan, inp)
+    ref = P.oracle_forward(wl, inp)
+    print(P.assert_parity(got, ref, P.TOL[wl.dtype], wl.name))
+
+
+@pytest.mark.parametrize("T", [1, 2, 17, 63, 64, 65, 255, 256, 257])
+@pytest.mark.parametrize("cid", [1, 3])
+def test_token_count_edges(cid, T):
+    base = workloads.WORKLOADS[cid]
+    wl = base.with_tokens(1, T) if cid == 1 else shaped(base.with_tokens(1, T), hidden=512)
+    inp = workloads.make_inputs(wl, seed=7 * T + cid)
+    with qkv.Plan.for_workload(wl, max_tokens=300) as plan:
+        got = run(plan, inp)
+    ref = P.oracle_forward(wl, inp)
+    P.assert_parity(got, ref, P.TOL[wl.dtype], f"{wl.name} T={T}")
+
+
+@pytest.mark.parametrize("nq,nkv,d", [(4, 4, 64), (8, 2, 128), (2, 1, 256), (6, 3, 8), (3, 1, 128)])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_head_shapes(nq, nkv, d, dtype):
+    wl = workloads.Workload(9, f"heads{nq}x{nkv}x{d}", 1, 100, 256, nq, nkv, d, True, 1e4, 1e-6, dtype, "per_seq")
+    inp = workloads.make_inputs(wl, seed=nq * 100 + nkv * 10 + d)
+    with qkv.Plan.for_workload(wl) as plan:
+        got = run(plan, inp)
+    P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL[dtype], wl.name)
+
+
+# ---------------------------------------------------------------- inputs the workloads cannot see
+
+def _pin_case(kind, dtype="bf16"):
+    wl = workloads.Workload(8, f"pin_{kind}", 1, 96, 512, 4, 2, 128, kind == "big_bias", 1e4, 1e-6, dtype,
+                            "per_seq")
+    inp = workloads.make_inputs(wl, seed=404)
+    g = torch.Generator().manual_seed(405)
+    dt = wl.torch_dtype
+    if kind == "row_scaled":
+        scale = 10.0 ** (torch.rand(wl.tokens, 1, generator=g) * 4 - 2)
+        inp["x"] = (inp["x"].float() * scale).to(dt)
+    elif kind == "small_rows":
+        inp["x"] = (inp["x"].float() * 1e-3).to(dt)
+    elif kind == "big_bias":
+        inp["bias"] = torch.randn(wl.n_total, generator=g).to(dt)
+    elif kind == "one_hot":
+        W = torch.zeros(wl.hidden, wl.n_total)
+        for j, (k0, n0) in enumerate([(0, 0), (511, wl.n_q - 1), (17, wl.n_q), (300, wl.n_total - 1)]):
+            W[k0, n0] = 1.0
+        inp["w_qkv"] = W.to(dt)
+    elif kind == "positions":
+        inp["pos"] = torch.tensor([0, -1, -32768, 2**31 - 1, -(2**31), 1, 65535, 4096] * 12, dtype=torch.int32)
+    return wl, inp
+
+
+@pytest.mark.parametrize("kind", ["row_scaled", "small_rows", "big_bias", "one_hot", "positions"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_pinning_inputs(kind, dtype):
+    wl, inp = _pin_case(kind, dtype)
+    with qkv.Plan.for_workload(wl) as plan:
+        got = run(plan, inp)
+    P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL[dtype], f"{kind}/{dtype}")
+
+
+def test_eps_is_applied():
+    """Rows with mean square ~1e-6: eps=1e-5 and eps=1e-6 give visibly different
+    outputs, and each matches the oracle with its own eps."""
+    wl, inp = _pin_case("small_rows", "fp32")
+    outs = []
+    for eps in (1e-6, 1e-5):
+        w2 = dataclasses.replace(wl, eps=eps)
+        with qkv.Plan.for_workload(w2) as plan:
+            got = run(plan, inp)
+        P.assert_parity(got, P.oracle_forward(w2, inp), P.TOL["fp32"], f"eps={eps}")
+        outs.append(got[2].float().cpu())
+    assert (outs[0] - outs[1]).abs().max() > 1e-2
+
+
+# ---------------------------------------------------------------- row reduction alone
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_rms_inv_step(cid):
+    from oracle import qkv_oracle
+    wl = workloads.WORKLOADS[cid]
+    inp = workloads.make_inputs(wl)
+    with qkv.Plan.for_workload(wl) as plan:
+        r = plan.rms_inv(inp["x"].to(DEV))
+        torch.cuda.synchronize()
+    ref = qkv_oracle.inv_rms(P.to_f64(inp["x"]), wl.eps)
+    err = np.max(np.abs(P.to_f64(r) - ref) / np.abs(ref))
+    assert err < 2e-6, err
+
+
+# ---------------------------------------------------------------- properties at full size
+
+@pytest.mark.parametrize("cid", [2, 4])
+def test_deterministic(cid):
+    wl = workloads.WORKLOADS[cid]
+    inp = workloads.make_inputs(wl)
+    with qkv.Plan.for_workload(wl) as plan:
+        a = [t.clone() for t in run(plan, inp)]
+        b = run(plan, inp)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+
+
+def test_side_stream_and_output_reuse():
+    wl = workloads.WORKLOADS[3].with_tokens(1, 384)
+    inp = workloads.make_inputs(wl, seed=5)
+    s = torch.cuda.Stream()
+    with qkv.Plan.for_workload(wl) as plan:
+        with torch.cuda.stream(s):
+            got = run(plan, inp, stream=s)
+    P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], "side stream")
+
+
+# ---------------------------------------------------------------- boundary behaviour with a device
+
+def test_forward_argument_errors():
+    wl = workloads.WORKLOADS[3].with_tokens(1, 64)
+    inp = workloads.make_inputs(wl)
+    lib = qkv.load_library()
+    with qkv.Plan.for_workload(wl) as plan:
+        x = inp["x"].to(DEV)
+        w = inp["w_norm"].to(DEV)
+        W = inp["w_qkv"].to(DEV)
+        pos = inp["pos"].to(DEV)
+        q = torch.empty(64, wl.n_q, dtype=torch.bfloat16, device=DEV)
+        k = torch.empty(64, wl.n_kv, dtype=torch.bfloat16, device=DEV)
+        v = torch.empty(64, wl.n_kv, dtype=torch.bfloat16, device=DEV)
+        P_ = lambda t: t.data_ptr()
+        h = plan.handle
+        ok = lambda: lib.qkv_forward(h, 64, P_(x), P_(w), P_(W), None, P_(pos), P_(q), P_(k), P_(v), None)
+        assert ok() == qkv.QKV_OK
+        assert lib.qkv_forward(h, 65, P_(x), P_(w), P_(W), None, P_(pos), P_(q), P_(k), P_(v), None) == 1
+        assert lib.qkv_forward(h, -1, P_(x), P_(w), P_(W), None, P_(pos), P_(q), P_(k), P_(v), None) == 1
+        assert lib.qkv_forward(h, 64, P_(x) + 2, P_(w), P_(W), None, P_(pos), P_(q), P_(k), P_(v), None) == 1
+        assert lib.qkv_forward(h, 64, P_(x), P_(w), P_(W), P_(w), P_(pos), P_(q), P_(k), P_(v), None) == 1
+        assert lib.qkv_forward(h, 64, P_(x), P_(w), P_(W), None, None, P_(q), P_(k), P_(v), None) == 1
+        assert lib.qkv_forward(h, 0, None, None, None, None, None, None, None, None, None) == qkv.QKV_OK
+        torch.cuda.synchronize()
+
+
+def test_variant_names():
+    for cid in (1, 2, 3, 4, 5):
+        wl = workloads.WORKLOADS[cid]
+        with qkv.Plan.for_workload(wl) as plan:
+            v = plan.variant(wl.tokens)
+            print(wl.name, v)
+            if wl.dtype == "fp32":
+                assert v == "generic"

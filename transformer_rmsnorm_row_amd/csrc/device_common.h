@@ -1,0 +1,69 @@
+// Device-side helpers shared by the kernels of the fused attention-input chain
+// (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qkv {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a gfx9-family buffer resource: 32-bit data format, raw (unswizzled)
+// addressing.  With stride 0 the record count is a byte bound; loads beyond it
+// return zero and stores beyond it are dropped.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufferWord3);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+  return __builtin_bit_cast(u32x4, v);
+}
+
+__device__ __forceinline__ void buf_store16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, 0);
+}
+
+// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even and keeps
+// NaN a NaN (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 a = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, a);
+}
+
+// cos and sin of the rotary angle pos * theta^(-2i/d).  `rev` is that frequency in
+// revolutions per position, theta^(-2i/d) / (2 pi), prepared in fp64 on the host.
+// The product and its reduction to [-1/2, 1/2] revolution are done in fp64, so
+// positions up to 2^31 keep their angle to ~1e-9 rad; the reduced angle is then
+// evaluated by the device math library's sincospi in fp32.
+__device__ __forceinline__ void rope_cos_sin(int32_t pos, double rev, float& c, float& s) {
+  double turns = (double)pos * rev;
+  double red = turns - rint(turns);            // [-0.5, 0.5] revolution
+  float half_turns = (float)(2.0 * red);       // angle / pi in [-1, 1]
+  sincospif(half_turns, &s, &c);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace qkv

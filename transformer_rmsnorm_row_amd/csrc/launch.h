@@ -1,0 +1,34 @@
+// Host-side launchers of the kernels behind the C ABI (internal; not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qkv {
+
+// Everything one forward needs, resolved by the host API after validation.
+struct ForwardArgs {
+  const void* x;
+  const void* w_norm;
+  const void* w;
+  const void* bias;        // nullptr when the plan has no bias
+  const int32_t* pos;
+  void* q;
+  void* k;
+  void* v;
+  float* inv_rms;          // scratch [T] fp32
+  const double* rev_freq;  // [head_dim/2] rotary frequencies, revolutions per position
+  float* partials;         // decode scratch
+  uint32_t* counters;      // decode scratch
+  int T, H, N, Nq, Nkv, d;
+  float eps;
+  bool bf16;
+};
+
+hipError_t launch_inv_rms(const void* x, float* inv_rms, int T, int H, float eps, bool bf16,
+                          hipStream_t stream);
+hipError_t launch_generic(const ForwardArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
+bool prefill_supports(int H, int N, int Nq, int Nkv, int d);
+
+}  // namespace qkv

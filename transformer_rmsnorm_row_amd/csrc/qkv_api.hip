@@ -1,0 +1,253 @@
+// C ABI of the fused attention-input library: plan management, argument
+// validation and kernel selection.  Declarations and the contract of every entry
+// point are in include/qkv.h.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <unordered_set>
+
+#include <hip/hip_runtime.h>
+
+#include "qkv.h"
+#include "launch.h"
+
+namespace {
+
+constexpr uint64_t kPlanMagic = 0x514b564d49333535ull;  // "QKVMI355"
+
+struct Plan {
+  uint64_t magic;
+  qkv_plan_desc desc;
+  int device;
+  int N, Nq, Nkv;
+  bool bf16;
+  bool prefill_ok;
+  float* inv_rms;     // [max_tokens]
+  double* rev_freq;   // [head_dim/2]
+  float* partials;    // decode partial sums
+  uint32_t* counters; // decode arrival counters
+};
+
+std::mutex g_mu;
+std::unordered_set<const void*> g_live;
+
+bool is_live(const void* p) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return g_live.count(p) != 0;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kMaxBytes = (int64_t)1 << 31;  // 32-bit byte offsets in every kernel
+
+qkv_status check_desc(const qkv_plan_desc* d) {
+  if (!d) return QKV_ERR_INVALID_ARG;
+  if (d->max_tokens < 1) return QKV_ERR_INVALID_ARG;
+  if (d->hidden < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 2) return QKV_ERR_INVALID_ARG;
+  if (d->head_dim % 2 != 0) return QKV_ERR_INVALID_ARG;
+  if (d->num_q_heads % d->num_kv_heads != 0) return QKV_ERR_INVALID_ARG;
+  if (d->dtype != QKV_F32 && d->dtype != QKV_BF16) return QKV_ERR_INVALID_ARG;
+  if (d->has_bias != 0 && d->has_bias != 1) return QKV_ERR_INVALID_ARG;
+  if (!std::isfinite(d->eps) || d->eps < 0.0) return QKV_ERR_INVALID_ARG;
+  if (!std::isfinite(d->rope_theta) || d->rope_theta <= 0.0) return QKV_ERR_INVALID_ARG;
+  if (d->hidden % 8 != 0) return QKV_ERR_UNSUPPORTED;
+  if (d->head_dim % 8 != 0) return QKV_ERR_UNSUPPORTED;
+  const int64_t elem = d->dtype == QKV_BF16 ? 2 : 4;
+  const int64_t N = (int64_t)(d->num_q_heads + 2 * (int64_t)d->num_kv_heads) * d->head_dim;
+  if (N >= kMaxBytes) return QKV_ERR_UNSUPPORTED;
+  const int64_t widest = N > d->hidden ? N : d->hidden;
+  if (d->max_tokens >= kMaxBytes / (widest * elem)) return QKV_ERR_UNSUPPORTED;
+  if ((int64_t)d->hidden * N * elem >= kMaxBytes) return QKV_ERR_UNSUPPORTED;
+  return QKV_OK;
+}
+
+Plan* as_plan(qkv_plan p) {
+  if (!p || !is_live(p)) return nullptr;
+  Plan* pl = reinterpret_cast<Plan*>(p);
+  return pl->magic == kPlanMagic ? pl : nullptr;
+}
+
+qkv_status check_device(const Plan* pl) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return QKV_ERR_HIP;
+  return dev == pl->device ? QKV_OK : QKV_ERR_INVALID_ARG;
+}
+
+void free_scratch(Plan* pl) {
+  if (pl->inv_rms) (void)hipFree(pl->inv_rms);
+  if (pl->rev_freq) (void)hipFree(pl->rev_freq);
+  if (pl->partials) (void)hipFree(pl->partials);
+  if (pl->counters) (void)hipFree(pl->counters);
+  pl->inv_rms = nullptr;
+  pl->rev_freq = nullptr;
+  pl->partials = nullptr;
+  pl->counters = nullptr;
+}
+
+int choose_variant(const Plan* pl, int64_t T) {
+  (void)T;
+  if (pl->bf16 && pl->prefill_ok) return QKV_VARIANT_PREFILL;
+  return QKV_VARIANT_GENERIC;
+}
+
+}  // namespace
+
+extern "C" {
+
+qkv_status qkv_plan_create(const qkv_plan_desc* desc, qkv_plan* out_plan) {
+  if (!out_plan) return QKV_ERR_INVALID_ARG;
+  *out_plan = nullptr;
+  qkv_status st = check_desc(desc);
+  if (st != QKV_OK) return st;
+
+  Plan* pl = new (std::nothrow) Plan();
+  if (!pl) return QKV_ERR_OUT_OF_MEMORY;
+  std::memset(pl, 0, sizeof(*pl));
+  pl->magic = kPlanMagic;
+  pl->desc = *desc;
+  pl->Nq = desc->num_q_heads * desc->head_dim;
+  pl->Nkv = desc->num_kv_heads * desc->head_dim;
+  pl->N = pl->Nq + 2 * pl->Nkv;
+  pl->bf16 = desc->dtype == QKV_BF16;
+  pl->prefill_ok = pl->bf16 && qkv::prefill_supports(desc->hidden, pl->N, pl->Nq, pl->Nkv, desc->head_dim);
+
+  if (hipGetDevice(&pl->device) != hipSuccess) {
+    delete pl;
+    return QKV_ERR_HIP;
+  }
+  const int half = desc->head_dim / 2;
+  if (hipMalloc(&pl->inv_rms, sizeof(float) * (size_t)desc->max_tokens) != hipSuccess ||
+      hipMalloc(&pl->rev_freq, sizeof(double) * (size_t)half) != hipSuccess) {
+    free_scratch(pl);
+    delete pl;
+    (void)hipGetLastError();
+    return QKV_ERR_OUT_OF_MEMORY;
+  }
+  // Rotary frequencies theta^(-2i/d), stored in revolutions per position so the
+  // kernels can reduce the angle exactly with a rounding of the turn count.
+  double host_rev[1024];
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < half && i < 1024; ++i)
+    host_rev[i] = std::pow(desc->rope_theta, -2.0 * (double)i / (double)desc->head_dim) / two_pi;
+  if (half > 1024 ||
+      hipMemcpy(pl->rev_freq, host_rev, sizeof(double) * (size_t)half, hipMemcpyHostToDevice) != hipSuccess) {
+    free_scratch(pl);
+    delete pl;
+    return half > 1024 ? QKV_ERR_UNSUPPORTED : QKV_ERR_HIP;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_live.insert(pl);
+  }
+  *out_plan = reinterpret_cast<qkv_plan>(pl);
+  return QKV_OK;
+}
+
+qkv_status qkv_plan_variant(qkv_plan plan, int64_t num_tokens, int32_t* variant) {
+  Plan* pl = as_plan(plan);
+  if (!pl || !variant || num_tokens < 1 || num_tokens > pl->desc.max_tokens) return QKV_ERR_INVALID_ARG;
+  *variant = choose_variant(pl, num_tokens);
+  return QKV_OK;
+}
+
+qkv_status qkv_forward(qkv_plan plan, int64_t num_tokens, const void* x, const void* w_norm, const void* w_qkv,
+                       const void* bias, const int32_t* pos, void* q, void* k, void* v, void* stream) {
+  Plan* pl = as_plan(plan);
+  if (!pl) return QKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return QKV_OK;
+  if (num_tokens < 0 || num_tokens > pl->desc.max_tokens) return QKV_ERR_INVALID_ARG;
+  if (!x || !w_norm || !w_qkv || !pos || !q || !k || !v) return QKV_ERR_INVALID_ARG;
+  if ((bias != nullptr) != (pl->desc.has_bias == 1)) return QKV_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w_norm, 16) || !aligned(w_qkv, 16) || !aligned(q, 16) || !aligned(k, 16) ||
+      !aligned(v, 16) || !aligned(pos, 4) || (bias && !aligned(bias, 16)))
+    return QKV_ERR_INVALID_ARG;
+  qkv_status st = check_device(pl);
+  if (st != QKV_OK) return st;
+
+  qkv::ForwardArgs a{};
+  a.x = x;
+  a.w_norm = w_norm;
+  a.w = w_qkv;
+  a.bias = bias;
+  a.pos = pos;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.inv_rms = pl->inv_rms;
+  a.rev_freq = pl->rev_freq;
+  a.partials = pl->partials;
+  a.counters = pl->counters;
+  a.T = (int)num_tokens;
+  a.H = pl->desc.hidden;
+  a.N = pl->N;
+  a.Nq = pl->Nq;
+  a.Nkv = pl->Nkv;
+  a.d = pl->desc.head_dim;
+  a.eps = (float)pl->desc.eps;
+  a.bf16 = pl->bf16;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  hipError_t e;
+  switch (choose_variant(pl, num_tokens)) {
+    case QKV_VARIANT_PREFILL:
+      e = qkv::launch_prefill(a, s);
+      break;
+    default:
+      e = qkv::launch_generic(a, s);
+      break;
+  }
+  return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
+}
+
+qkv_status qkv_rms_inv(qkv_plan plan, int64_t num_tokens, const void* x, float* inv_rms, void* stream) {
+  Plan* pl = as_plan(plan);
+  if (!pl) return QKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return QKV_OK;
+  if (num_tokens < 0 || num_tokens > pl->desc.max_tokens) return QKV_ERR_INVALID_ARG;
+  if (!x || !inv_rms || !aligned(x, 16) || !aligned(inv_rms, 4)) return QKV_ERR_INVALID_ARG;
+  qkv_status st = check_device(pl);
+  if (st != QKV_OK) return st;
+  hipError_t e = qkv::launch_inv_rms(x, inv_rms, (int)num_tokens, pl->desc.hidden, (float)pl->desc.eps, pl->bf16,
+                                     reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
+}
+
+qkv_status qkv_plan_destroy(qkv_plan plan) {
+  if (!plan) return QKV_OK;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_live.erase(plan)) return QKV_ERR_INVALID_ARG;
+  }
+  Plan* pl = reinterpret_cast<Plan*>(plan);
+  int prev = -1;
+  bool switched = hipGetDevice(&prev) == hipSuccess && prev != pl->device && hipSetDevice(pl->device) == hipSuccess;
+  (void)hipDeviceSynchronize();
+  free_scratch(pl);
+  if (switched) (void)hipSetDevice(prev);
+  pl->magic = 0;
+  delete pl;
+  return QKV_OK;
+}
+
+const char* qkv_status_string(qkv_status status) {
+  switch (status) {
+    case QKV_OK: return "ok";
+    case QKV_ERR_INVALID_ARG: return "invalid argument";
+    case QKV_ERR_UNSUPPORTED: return "unsupported shape or configuration";
+    case QKV_ERR_HIP: return "HIP runtime error";
+    case QKV_ERR_OUT_OF_MEMORY: return "out of device memory";
+  }
+  return "unknown status";
+}
+
+const char* qkv_variant_name(int32_t variant) {
+  switch (variant) {
+    case QKV_VARIANT_GENERIC: return "generic";
+    case QKV_VARIANT_PREFILL: return "prefill";
+    case QKV_VARIANT_DECODE: return "decode";
+  }
+  return "unknown";
+}
+
+}  // extern "C"
