@@ -65,6 +65,20 @@ __device__ __forceinline__ float turn_fraction(int32_t pos, double rev) {
   return (float)(t - floor(t));
 }
 
+// Interleave the 16 MFMAs of a K substep with the VALU, LDS and VMEM work issued
+// alongside them, so the matrix pipe is not left waiting behind the rest.
+template <int kValuPerMfma, int kDsReads, int kDsWrites, int kVmemReads>
+__device__ __forceinline__ void sched_substep() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (kValuPerMfma > 0) __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+    if (i < kDsReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i >= 4 && i - 4 < kDsWrites) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    if (i >= 6 && i - 6 < kVmemReads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+}
+
 __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
   int32_t* s_pos = reinterpret_cast<int32_t*>(smem + kMainBytes);
@@ -85,7 +99,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tile
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int wm = wave >> 1, wn = wave & 1;
   const int H = a.H, N = a.N, T = a.T;
 
@@ -133,14 +148,19 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tile
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   u32x4 ga[8], gb[8], gw;
-  auto gload = [&](int k0) {
+  // Loads of a K slice.  Past the end of K they read zeros (out of the buffer's
+  // range) or rows that are never used, so the loop body needs no branch.
+  auto gload_a = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) ga[j] = buf_load16(rx, a_goff + j * a_gstep + (uint32_t)k0 * 2u);
     gw = buf_load16(rwn, ((uint32_t)k0 + kc * 8u) * 2u);
+  };
+  auto gload_b = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) gb[j] = buf_load16(rw, b_goff + ((uint32_t)k0 + j) * b_gstep);
   };
-  auto lstore = [&](uint8_t* As, uint8_t* Bs) {
+  // x rows j0..j1-1 of the slice: scale by the norm weight in fp32, round to bf16.
+  auto lstore_a = [&](uint8_t* As, int j0, int j1) {
     float wf[8];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -148,14 +168,17 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tile
       wf[2 * c + 1] = bf16_hi(gw[c]);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = j0; j < j1; ++j) {
       u32x4 o;
 #pragma unroll
       for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(bf16_lo(ga[j][c]) * wf[2 * c], bf16_hi(ga[j][c]) * wf[2 * c + 1]);
       lds_write16(As, a_soff[j], o);
     }
+  };
+  // weight columns 8bc + jj (jj0..jj1-1) of the slice, transposed to [n][k].
+  auto lstore_b = [&](uint8_t* Bs, int jj0, int jj1) {
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
+    for (int jj = jj0; jj < jj1; ++jj) {
       const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
       u32x4 o;
 #pragma unroll
@@ -163,35 +186,68 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tile
       lds_write16(Bs, b_soff[jj], o);
     }
   };
-
-  const int nk = H / BK;
-  gload(0);
-  lstore(smem, smem + kTile);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    uint8_t* As = smem + (kt & 1) * 2 * kTile;
-    uint8_t* Bs = As + kTile;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  auto read_frags = [&](const uint8_t* As, const uint8_t* Bs, int ks, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = __builtin_bit_cast(bf16x8, lds_read16(As, a_roff[i][ks]));
-        bf[i] = __builtin_bit_cast(bf16x8, lds_read16(Bs, b_roff[i][ks]));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      fa[i] = __builtin_bit_cast(bf16x8, lds_read16(As, a_roff[i][ks]));
+      fb[i] = __builtin_bit_cast(bf16x8, lds_read16(Bs, b_roff[i][ks]));
     }
-    if (kt + 1 < nk) {
-      uint8_t* An = smem + ((kt + 1) & 1) * 2 * kTile;
-      lstore(An, An + kTile);
-    }
+  };
+  auto mfmas = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  uint8_t* const A0 = smem;
+  uint8_t* const B0 = smem + kTile;
+  uint8_t* const A1 = smem + 2 * kTile;
+  uint8_t* const B1 = smem + 3 * kTile;
+
+  // One K slice from (Ac, Bc) while slice kt+1 goes from registers into (An, Bn)
+  // and slice kt+2 is fetched into the registers.
+  auto body = [&](const uint8_t* Ac, const uint8_t* Bc, uint8_t* An, uint8_t* Bn, int kt) {
+    read_frags(Ac, Bc, 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    lstore_a(An, 0, 4);
+    sched_substep<5, 8, 4, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(Ac, Bc, 2, fa0, fb0);
+    mfmas(fa1, fb1);
+    lstore_a(An, 4, 8);
+    gload_a((kt + 2) * BK);
+    sched_substep<5, 8, 4, 9>();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(Ac, Bc, 3, fa1, fb1);
+    mfmas(fa0, fb0);
+    lstore_b(Bn, 0, 4);
+    sched_substep<1, 8, 4, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fa1, fb1);
+    lstore_b(Bn, 4, 8);
+    gload_b((kt + 2) * BK);
+    sched_substep<1, 0, 4, 8>();
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    read_frags(An, Bn, 0, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const int nk = H / BK;  // even
+  gload_a(0);
+  gload_b(0);
+  lstore_a(A0, 0, 8);
+  lstore_b(B0, 0, 8);
+  gload_a(BK);
+  gload_b(BK);
+  __syncthreads();
+  read_frags(A0, B0, 0, fa0, fb0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    body(A0, B0, A1, B1, kt);
+    body(A1, B1, A0, B0, kt + 1);
   }
+  __syncthreads();
 
   // ---- epilogue: scale, bias, rotate, stage as bf16, store
   const int col0 = n0 + wn * 128;  // first column of this wave's head
@@ -255,7 +311,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tile
 }  // namespace
 
 bool prefill_supports(int H, int N, int Nq, int Nkv, int d) {
-  return d == 128 && H % BK == 0 && N % BN == 0 && Nq % 128 == 0 && Nkv % 128 == 0;
+  return d == 128 && H % (2 * BK) == 0 && N % BN == 0 && Nq % 128 == 0 && Nkv % 128 == 0;
 }
 
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream) {
