@@ -41,17 +41,39 @@ namespace {
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int kTile = BM * BK * 2;                 // bytes of one [256][64] bf16 tile
+constexpr int kTile = BM * BK * 2;                 // bytes of one [256][64] bf16 tile (A or B)
+constexpr int kBStages = 3;                        // weight slices in flight (global -> LDS directly)
+constexpr int kAStages = 2;                        // converted activation slices
+constexpr int kBBase = 0;
+constexpr int kABase = kBStages * kTile;
+constexpr int kLds = (kBStages + kAStages) * kTile;  // 160 KB
 constexpr int kStagePitch = 272;                   // 128 bf16 + 16 B pad per staged output row
 constexpr int kStageBytes = 128 * kStagePitch;     // one wave's 128 x 128 output block
-constexpr int kMainBytes = 4 * kStageBytes > 4 * kTile ? 4 * kStageBytes : 4 * kTile;
-constexpr int kLds = kMainBytes + BM * 8;          // + per-row pos and 1/rms
+constexpr int kRowInfo = 4 * kStageBytes;          // per-row pos and 1/rms after the staging area
+static_assert(kRowInfo + BM * 8 <= kLds, "epilogue staging must fit in the tile memory");
 constexpr int kGroupM = 4;
 
-// LDS address of 16-byte chunk `chunk` (0..7) of row `row` in a [256][64] bf16 tile.
+// LDS address of 16-byte chunk `chunk` (0..7) of row `row` in a [256][64] bf16
+// activation tile (row = token, 64 k per row).
 __device__ __forceinline__ uint32_t tile_off(uint32_t row, uint32_t chunk) {
   return row * 128u + ((chunk ^ ((row ^ (row >> 3)) & 7u)) << 4);
 }
+// The weight slice stays [64 k][256 n] (512 B rows) as loaded; 16-byte chunk c of
+// row k sits at chunk c ^ 4*(k mod 4), which spreads the 4-row x 16-column blocks
+// of a transpose read over all banks.
+__device__ __forceinline__ uint32_t wchunk(uint32_t k, uint32_t c) { return c ^ ((k & 3u) << 2); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ u32x4 lds_read16(const uint8_t* base, uint32_t off) {
   return *reinterpret_cast<const u32x4*>(base + off);
@@ -81,8 +103,6 @@ __device__ __forceinline__ void sched_substep() {
 
 __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
-  int32_t* s_pos = reinterpret_cast<int32_t*>(smem + kMainBytes);
-  float* s_rinv = reinterpret_cast<float*>(smem + kMainBytes + BM * 4);
 
   // ---- tile selection: XCD-contiguous numbering, then groups of kGroupM row panels
   const int G = tiles_m * tiles_n;
@@ -104,40 +124,63 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tile
   const int wm = wave >> 1, wn = wave & 1;
   const int H = a.H, N = a.N, T = a.T;
 
-  {
-    int t = m0 + tid;
-    s_pos[tid] = t < T ? a.pos[t] : 0;
-    s_rinv[tid] = t < T ? a.inv_rms[t] : 0.f;
-  }
-
   const auto rx = make_rsrc(a.x, (uint32_t)T * (uint32_t)H * 2u);
   const auto rwn = make_rsrc(a.w_norm, (uint32_t)H * 2u);
-  const auto rw = make_rsrc(a.w, (uint32_t)H * (uint32_t)N * 2u);
 
-  // ---- per-thread global load coordinates
-  const uint32_t kc = tid & 7, ar = tid >> 3;             // A: chunk kc of rows ar + 32j
-  const uint32_t bc = tid & 31, bg = tid >> 5;            // B: cols 8bc.., rows 8bg + j
+  // ---- activation slice (registers -> LDS): thread owns chunk kc of rows ar + 32j
+  const uint32_t kc = tid & 7, ar = tid >> 3;
   const uint32_t a_goff = ((uint32_t)(m0 + ar) * H + kc * 8u) * 2u;
   const uint32_t a_gstep = 32u * H * 2u;
-  const uint32_t b_goff = (8u * bg * N + n0 + 8u * bc) * 2u;
-  const uint32_t b_gstep = (uint32_t)N * 2u;
-
-  uint32_t a_soff[8], b_soff[8];
+  uint32_t a_soff[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    a_soff[j] = tile_off(ar + 32u * j, kc);
-    b_soff[j] = tile_off(8u * bc + j, bg);
+  for (int j = 0; j < 8; ++j) a_soff[j] = kABase + tile_off(ar + 32u * j, kc);
+
+  // ---- weight slice (global -> LDS directly): wave loads rows 16*wave + 2i (+1),
+  // each instruction one 1 KB run of LDS = two 512 B rows; lane l fills physical
+  // chunk l % 32 of row 2i + l / 32, i.e. logical chunk wchunk(row, l % 32).
+  uint32_t b_voff[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const uint32_t krow = 2u * par + (lane >> 5);  // row within the 4-row swizzle period
+    b_voff[par] = ((16u * wave + krow) * N + n0 + 8u * wchunk(krow, lane & 31)) * 2u;
   }
-  // ---- per-lane fragment read offsets
+  // Issued as inline assembly: the compiler cannot tell that a stage being
+  // filled is never the one being read, and would otherwise drain every load
+  // before each LDS read.  The waits are explicit (wait_vmcnt before barriers).
+  const uint64_t wbase = reinterpret_cast<uint64_t>(a.w);
+  const u32x4 w_rsrc = {(uint32_t)wbase, (uint32_t)(wbase >> 32), (uint32_t)H * (uint32_t)N * 2u,
+                        (uint32_t)kBufferWord3};
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  auto dma_b = [&](int k0, int stage) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + kBBase + stage * kTile + (16 * wave + 2 * i) * 512);
+      // the whole offset goes in the per-lane operand so the buffer's range check
+      // (zero fill past the end of the weight) sees all of it
+      const uint32_t voff = b_voff[i & 1] + ((uint32_t)k0 + 2u * (i & ~1)) * (uint32_t)N * 2u;
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(voff), "s"(w_rsrc)
+                   : "m0");
+    }
+  };
+
+  // ---- fragment read offsets
   const uint32_t fl = lane & 31, fh = lane >> 5;
-  uint32_t a_roff[4][4], b_roff[4][4];
+  uint32_t a_roff[4][4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      a_roff[rb][ks] = tile_off(wm * 128u + rb * 32u + fl, ks * 2u + fh);
-      b_roff[rb][ks] = tile_off(wn * 128u + rb * 32u + fl, ks * 2u + fh);
-    }
+    for (int ks = 0; ks < 4; ++ks) a_roff[rb][ks] = kABase + tile_off(wm * 128u + rb * 32u + fl, ks * 2u + fh);
+  // transpose reads of the weight: 16-lane group g covers k rows 8(g/2) + 4h + 0..3
+  // and columns 16(g%2) + 0..15 of a 32-column block; lane j of the group points at
+  // row j/4, columns 4(j%4)..+3.
+  const uint32_t tg = lane >> 4, tj = lane & 15;
+  uint32_t b_roff[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const uint32_t krow = 8u * (tg >> 1) + (tj >> 2);
+    const uint32_t col = wn * 128u + cb * 32u + 16u * (tg & 1) + 4u * (tj & 3);
+    b_roff[cb] = krow * 512u + wchunk(krow, col >> 3) * 16u + (col & 7u) * 2u;
+  }
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -147,105 +190,128 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tile
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4 ga[8], gb[8], gw;
-  // Loads of a K slice.  Past the end of K they read zeros (out of the buffer's
-  // range) or rows that are never used, so the loop body needs no branch.
-  auto gload_a = [&](int k0) {
+  u32x4 ga[2][8], gw[2];
+  // Loads past the end of K read zeros (outside the buffer's range) or rows that
+  // are never used, so the loop body needs no branch.
+  auto gload_rows = [&](int set, int k0, int j0, int j1) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ga[j] = buf_load16(rx, a_goff + j * a_gstep + (uint32_t)k0 * 2u);
-    gw = buf_load16(rwn, ((uint32_t)k0 + kc * 8u) * 2u);
+    for (int j = j0; j < j1; ++j) ga[set][j] = buf_load16(rx, a_goff + j * a_gstep + (uint32_t)k0 * 2u);
   };
-  auto gload_b = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) gb[j] = buf_load16(rw, b_goff + ((uint32_t)k0 + j) * b_gstep);
-  };
-  // x rows j0..j1-1 of the slice: scale by the norm weight in fp32, round to bf16.
-  auto lstore_a = [&](uint8_t* As, int j0, int j1) {
+  auto gload_w = [&](int set, int k0) { gw[set] = buf_load16(rwn, ((uint32_t)k0 + kc * 8u) * 2u); };
+  // rows j0..j1-1 of a slice: x * norm weight in fp32, rounded once to bf16, into LDS
+  auto convert_rows = [&](int set, int stage, int j0, int j1) {
     float wf[8];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      wf[2 * c] = bf16_lo(gw[c]);
-      wf[2 * c + 1] = bf16_hi(gw[c]);
+      wf[2 * c] = bf16_lo(gw[set][c]);
+      wf[2 * c + 1] = bf16_hi(gw[set][c]);
     }
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
       u32x4 o;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(bf16_lo(ga[j][c]) * wf[2 * c], bf16_hi(ga[j][c]) * wf[2 * c + 1]);
-      lds_write16(As, a_soff[j], o);
+      for (int c = 0; c < 4; ++c)
+        o[c] = pack_bf16x2(bf16_lo(ga[set][j][c]) * wf[2 * c], bf16_hi(ga[set][j][c]) * wf[2 * c + 1]);
+      lds_write16(smem, a_soff[j] + stage * kTile, o);
     }
   };
-  // weight columns 8bc + jj (jj0..jj1-1) of the slice, transposed to [n][k].
-  auto lstore_b = [&](uint8_t* Bs, int jj0, int jj1) {
+
+  bf16x8 fa[2][4], fb[2][4];
+  auto read_frags = [&](int astage, uint32_t bbase, int ks, int buf) {
 #pragma unroll
-    for (int jj = jj0; jj < jj1; ++jj) {
-      const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 o;
+    for (int i = 0; i < 4; ++i) fa[buf][i] = __builtin_bit_cast(bf16x8, lds_read16(smem, a_roff[i][ks] + astage * kTile));
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) o[qd] = __builtin_amdgcn_perm(gb[2 * qd + 1][jj >> 1], gb[2 * qd][jj >> 1], sel);
-      lds_write16(Bs, b_soff[jj], o);
+    for (int cb = 0; cb < 4; ++cb) {
+      const uint8_t* p = smem + bbase + b_roff[cb] + ks * 16 * 512;
+      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
+      fb[buf][cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
-  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-  auto read_frags = [&](const uint8_t* As, const uint8_t* Bs, int ks, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[i] = __builtin_bit_cast(bf16x8, lds_read16(As, a_roff[i][ks]));
-      fb[i] = __builtin_bit_cast(bf16x8, lds_read16(Bs, b_roff[i][ks]));
-    }
-  };
-  auto mfmas = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+  auto mfmas = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
   };
-  uint8_t* const A0 = smem;
-  uint8_t* const B0 = smem + kTile;
-  uint8_t* const A1 = smem + 2 * kTile;
-  uint8_t* const B1 = smem + 3 * kTile;
 
-  // One K slice from (Ac, Bc) while slice kt+1 goes from registers into (An, Bn)
-  // and slice kt+2 is fetched into the registers.
-  auto body = [&](const uint8_t* Ac, const uint8_t* Bc, uint8_t* An, uint8_t* Bn, int kt) {
-    read_frags(Ac, Bc, 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    lstore_a(An, 0, 4);
-    sched_substep<5, 8, 4, 0>();
+  // One K slice kt: MFMAs from A stage (kt % 2) and B stage bcur; meanwhile the
+  // weight slice kt+2 streams into B stage bnext2, activation slice kt+1 (register
+  // set `cs`) is converted into A stage (kt+1) % 2, and activation slice kt+3 is
+  // loaded into the freed register set.
+  auto body = [&](int kt, int as, int cs, uint32_t bcur, int bnext2) {
+    dma_b((kt + 2) * BK, bnext2);
+    read_frags(as, bcur, 1, 1);
+    mfmas(0);
+    convert_rows(cs, as ^ 1, 0, 2);
+    gload_rows(cs, (kt + 3) * BK, 0, 2);
+    sched_substep<3, 12, 2, 10>();
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(Ac, Bc, 2, fa0, fb0);
-    mfmas(fa1, fb1);
-    lstore_a(An, 4, 8);
-    gload_a((kt + 2) * BK);
-    sched_substep<5, 8, 4, 9>();
+    read_frags(as, bcur, 2, 0);
+    mfmas(1);
+    convert_rows(cs, as ^ 1, 2, 4);
+    gload_rows(cs, (kt + 3) * BK, 2, 4);
+    sched_substep<3, 12, 2, 2>();
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(Ac, Bc, 3, fa1, fb1);
-    mfmas(fa0, fb0);
-    lstore_b(Bn, 0, 4);
-    sched_substep<1, 8, 4, 0>();
+    read_frags(as, bcur, 3, 1);
+    mfmas(0);
+    convert_rows(cs, as ^ 1, 4, 6);
+    gload_rows(cs, (kt + 3) * BK, 4, 6);
+    sched_substep<3, 12, 2, 2>();
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa1, fb1);
-    lstore_b(Bn, 4, 8);
-    gload_b((kt + 2) * BK);
-    sched_substep<1, 0, 4, 8>();
+    mfmas(1);
+    convert_rows(cs, as ^ 1, 6, 8);
+    gload_rows(cs, (kt + 3) * BK, 6, 8);
+    gload_w(cs, (kt + 3) * BK);
+    sched_substep<3, 0, 2, 3>();
     __builtin_amdgcn_sched_barrier(0);
+    // the weight slice read next (issued one slice ago) must have landed: at least
+    // that slice's last 7 activation loads and this slice's 17 loads came after it
+    wait_vmcnt<24>();
     __syncthreads();
-    read_frags(An, Bn, 0, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
   const int nk = H / BK;  // even
-  gload_a(0);
-  gload_b(0);
-  lstore_a(A0, 0, 8);
-  lstore_b(B0, 0, 8);
-  gload_a(BK);
-  gload_b(BK);
+  // prologue: weight slices 0 and 1 in flight, activation slices 0..2 loaded,
+  // slice 0 converted
+  dma_b(0, 0);
+  dma_b(BK, 1);
+  gload_rows(0, 0, 0, 8);
+  gload_w(0, 0);
+  gload_rows(1, BK, 0, 8);
+  gload_w(1, BK);
+  convert_rows(0, 0, 0, 8);
+  gload_rows(0, 2 * BK, 0, 8);
+  gload_w(0, 2 * BK);
+  wait_vmcnt<0>();
   __syncthreads();
-  read_frags(A0, B0, 0, fa0, fb0);
+
+  uint32_t bcur = kBBase, bn1 = kBBase + kTile, bn2i = 2;
   for (int kt = 0; kt < nk; kt += 2) {
-    body(A0, B0, A1, B1, kt);
-    body(A1, B1, A0, B0, kt + 1);
+    read_frags(0, bcur, 0, 0);
+    body(kt, 0, 1, bcur, bn2i);
+    {  // rotate the three weight stages
+      uint32_t t = bcur; bcur = bn1; bn1 = kBBase + bn2i * kTile; (void)t;
+      bn2i = (bn2i == 2) ? 0 : bn2i + 1;
+    }
+    read_frags(1, bcur, 0, 0);
+    body(kt + 1, 1, 0, bcur, bn2i);
+    {
+      bcur = bn1; bn1 = kBBase + bn2i * kTile;
+      bn2i = (bn2i == 2) ? 0 : bn2i + 1;
+    }
+  }
+  // drain the weight loads that ran past the end before the tile memory is reused
+  wait_vmcnt<0>();
+  __syncthreads();
+  int32_t* s_pos = reinterpret_cast<int32_t*>(smem + kRowInfo);
+  float* s_rinv = reinterpret_cast<float*>(smem + kRowInfo + BM * 4);
+  {
+    int t = m0 + tid;
+    s_pos[tid] = t < T ? a.pos[t] : 0;
+    s_rinv[tid] = t < T ? a.inv_rms[t] : 0.f;
   }
   __syncthreads();
 
