@@ -224,6 +224,28 @@ def test_forward_argument_errors():
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("T", [1, 2, 17, 33, 63, 64])
+def test_decode_token_counts(T):
+    """The small-batch kernel at every token count it takes, GQA decode shape."""
+    wl = workloads.WORKLOADS[4].with_tokens(T, 1)
+    inp = workloads.make_inputs(wl, seed=900 + T)
+    with qkv.Plan.for_workload(wl, max_tokens=64) as plan:
+        assert plan.variant(T) == "decode"
+        got = run(plan, inp)
+    P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], f"decode T={T}")
+
+
+@pytest.mark.parametrize("hidden,nq,nkv,bias", [(4096, 32, 32, True), (2048, 16, 4, False), (8192, 8, 2, True)])
+def test_decode_shapes(hidden, nq, nkv, bias):
+    wl = workloads.Workload(10, f"decode_{hidden}_{nq}x{nkv}", 24, 1, hidden, nq, nkv, 128, bias, 1e4, 1e-6,
+                            "bf16", "uniform32768")
+    inp = workloads.make_inputs(wl, seed=hidden + nq)
+    with qkv.Plan.for_workload(wl) as plan:
+        assert plan.variant(wl.tokens) == "decode"
+        got = run(plan, inp)
+    P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], wl.name)
+
+
 def test_variant_names():
     for cid in (1, 2, 3, 4, 5):
         wl = workloads.WORKLOADS[cid]
@@ -232,3 +254,7 @@ def test_variant_names():
             print(wl.name, v)
             if wl.dtype == "fp32":
                 assert v == "generic"
+            elif wl.tokens <= 64:
+                assert v == "decode"
+            else:
+                assert v == "prefill"

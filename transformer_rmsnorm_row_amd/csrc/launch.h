@@ -30,5 +30,7 @@ hipError_t launch_inv_rms(const void* x, float* inv_rms, int T, int H, float eps
 hipError_t launch_generic(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
 bool prefill_supports(int H, int N, int Nq, int Nkv, int d);
+hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
+bool decode_supports(int T, int H, int N, int Nq, int Nkv, int d);
 
 }  // namespace qkv

@@ -23,6 +23,7 @@ struct Plan {
   int N, Nq, Nkv;
   bool bf16;
   bool prefill_ok;
+  bool decode_ok;   // shape supported by the decode kernel (for T <= its token capacity)
   float* inv_rms;     // [max_tokens]
   double* rev_freq;   // [head_dim/2]
   float* partials;    // decode partial sums
@@ -86,7 +87,9 @@ void free_scratch(Plan* pl) {
 }
 
 int choose_variant(const Plan* pl, int64_t T) {
-  (void)T;
+  if (pl->bf16 && pl->decode_ok &&
+      qkv::decode_supports((int)T, pl->desc.hidden, pl->N, pl->Nq, pl->Nkv, pl->desc.head_dim))
+    return QKV_VARIANT_DECODE;
   if (pl->bf16 && pl->prefill_ok) return QKV_VARIANT_PREFILL;
   return QKV_VARIANT_GENERIC;
 }
@@ -111,6 +114,7 @@ qkv_status qkv_plan_create(const qkv_plan_desc* desc, qkv_plan* out_plan) {
   pl->N = pl->Nq + 2 * pl->Nkv;
   pl->bf16 = desc->dtype == QKV_BF16;
   pl->prefill_ok = pl->bf16 && qkv::prefill_supports(desc->hidden, pl->N, pl->Nq, pl->Nkv, desc->head_dim);
+  pl->decode_ok = pl->bf16 && qkv::decode_supports(1, desc->hidden, pl->N, pl->Nq, pl->Nkv, desc->head_dim);
 
   if (hipGetDevice(&pl->device) != hipSuccess) {
     delete pl;
@@ -192,6 +196,9 @@ qkv_status qkv_forward(qkv_plan plan, int64_t num_tokens, const void* x, const v
   switch (choose_variant(pl, num_tokens)) {
     case QKV_VARIANT_PREFILL:
       e = qkv::launch_prefill(a, s);
+      break;
+    case QKV_VARIANT_DECODE:
+      e = qkv::launch_decode(a, s);
       break;
     default:
       e = qkv::launch_generic(a, s);
