@@ -4,26 +4,32 @@
 // Same method as the prefill kernel -- the fused RMSNorm + QKV projection + RoPE of
 // the page "Liger-Kernel底层优化：新一代内核级推理加速引擎介绍" (fused-kernel listing in
 // section "融合内核是如何工作的？来看一段简化版实现") -- in the regime that page's
-// section on the system stack singles out: per-query efficiency, where a layer step
-// is a handful of tokens and the weight read dominates.  With 64 tokens the weight
-// (H x N bf16) is ~97% of all bytes, so the kernel is bound by HBM bandwidth and is
-// organised to keep every byte of W in flight once:
+// discussion of where the library sits in the stack singles out: per-query
+// efficiency, where a step is a handful of tokens and the weight read dominates.
+// With 64 tokens the weight (H x N bf16) is ~97% of all bytes, so the kernel is
+// bound by HBM bandwidth and is laid out so that every weight byte is read once,
+// in full 256-byte rows, while the activations stay cheap:
 //
-//   * 4 workgroups per head, each owning columns 16q..16q+15 and 64+16q..64+16q+15 of
-//     one head, so both members of every rotation pair stay in one lane; the four
-//     workgroups of a head are numbered onto the same XCD, so each 128-byte weight
-//     line is fetched into that XCD's L2 once and read by all four.
-//   * 8 waves per workgroup split K; each wave streams its 32-row weight slices
-//     global -> LDS (buffer_load ... lds) through an 8-deep ring, and reads them back
-//     as MFMA B fragments with ds_read_b64_tr_b16.  Activations (x, 64 x 32 per step)
-//     come into registers 4 steps ahead, are multiplied by the norm weight and
-//     rounded once to bf16 (normalise-on-load), and their squares are summed on the
-//     way, so the RMS row reduction needs no separate pass over x.
-//   * v_mfma_f32_16x16x32_bf16 over 4 token blocks x 2 column blocks per step.
-//   * Partial sums of the 8 waves are added in LDS in a fixed order (deterministic);
-//     then 1/rms, bias, rotation with in-kernel cos/sin, one bf16 store.
-// All vector-memory instructions are issued as inline assembly and every wait is an
-// exact, compile-time vmcnt, so the compiler never drains the pipeline.
+//   * Work unit = one head (128 output columns, so both members of every rotation
+//     pair are in the unit) x one of S slices of the hidden dimension.  Splitting K
+//     keeps the per-workgroup share of x small (x is read once per unit), so the
+//     CU load path carries mostly weight bytes.  Units of the same K slice are
+//     numbered onto the same XCDs and share their x slice in L2.
+//   * 4 waves per unit split its K slice; each wave streams 32-row steps of the
+//     weight (32 x 128 bf16) and of x (64 x 32 bf16) global -> LDS with
+//     buffer_load ... lds through a 3-deep ring.  B fragments (weight) come back
+//     with ds_read_b64_tr_b16, A fragments (x) with ds_read_b128; each A element is
+//     multiplied by its norm weight and rounded once to bf16 (normalise-on-load)
+//     with masked v_dot2_f32_bf16, and the squares of x are summed with
+//     v_dot2_f32_bf16 on the raw values for the RMS row reduction.
+//   * v_mfma_f32_32x32x16_bf16, 2 token blocks x 4 column blocks per 16-wide k.
+//   * The 4 waves add their partial sums in LDS; each unit writes its fp32 partial
+//     (64 x 128) and its partial sums of squares to plan scratch and bumps the
+//     head's arrival counter.  The unit that arrives last adds the S partials in a
+//     fixed order (so results are deterministic), applies 1/rms, bias and the
+//     rotation with in-kernel cos/sin, stores bf16, and resets the counter.
+// All vector-memory instructions in the streaming loop are inline assembly with
+// exact, compile-time vmcnt waits, so the compiler never drains the pipeline.
 #include <type_traits>
 
 #include "device_common.h"
@@ -33,15 +39,20 @@ namespace qkv {
 
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kStepK = 32;                     // k rows per step
-constexpr int kRing = 8;                       // weight steps in flight per wave
-constexpr int kXDepth = 4;                     // activation steps in flight per wave
-constexpr int kStepBytes = kStepK * 64;        // 32 rows x 32 columns x 2 B
-constexpr int kWaveRing = kRing * kStepBytes;  // 16 KB
-constexpr int kLds = kWaves * kWaveRing;       // 128 KB
-constexpr int kTokens = 64;                    // token capacity (4 blocks of 16)
+constexpr int kStepK = 32;                        // k rows per step
+constexpr int kRing = 3;                          // steps in flight per wave
+constexpr int kCols = 128;                        // one head
+constexpr int kTokens = 64;                       // token capacity (2 blocks of 32)
+constexpr int kWBytes = kStepK * kCols * 2;       // 8 KB weight per step
+constexpr int kXBytes = kTokens * kStepK * 2;     // 4 KB activations per step
+constexpr int kSlot = kWBytes + kXBytes;          // 12 KB
+constexpr int kWaveRing = kRing * kSlot;          // 36 KB
+constexpr int kLds = kWaves * kWaveRing;          // 144 KB
+constexpr int kOpsPerStep = 8 + 4 + 2;            // weight DMA + x DMA + 2 norm-weight loads
+constexpr int kMaxSplit = 4;                      // K slices per head, at most
+static_assert(kWaves * kTokens * kCols * 4 + kWaves * kTokens * 4 <= kLds, "wave partials must fit in LDS");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -54,54 +65,26 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Issue order of vector-memory instructions (per wave):
-//   prologue: weight slices 0..kRing-1 (2 instructions each), then activation steps
-//             0..kXDepth-1 (5 each: 4 token blocks + the norm weight);
-//   step s:   activation step s+kXDepth, then weight slice s+kRing (when they exist).
-// These helpers count that sequence so each wait can name exactly how many younger
-// instructions may stay outstanding.
+// Vector-memory issue order per wave: steps 0..kRing-1 in the prologue, then
+// step s+kRing right after step s has been consumed.  Every step is kOpsPerStep
+// instructions, so at the start of step s the loads of the (min(kRing, NS-s)-1)
+// later steps may still be outstanding.
 template <int NS>
-struct Issue {
-  static constexpr int wops(int s) { return s < NS ? 2 : 0; }
-  static constexpr int xops(int s) { return s < NS ? 5 : 0; }
-  // index one past the last instruction of weight slice s / activation step s
-  static constexpr int w_end(int s) {
-    if (s < kRing) {
-      int n = 0;
-      for (int t = 0; t <= s; ++t) n += wops(t);
-      return n;
-    }
-    return step_begin(s - kRing) + xops(s - kRing + kXDepth) + wops(s);
-  }
-  static constexpr int x_end(int s) {
-    if (s < kXDepth) {
-      int n = 0;
-      for (int t = 0; t < kRing; ++t) n += wops(t);
-      for (int t = 0; t <= s; ++t) n += xops(t);
-      return n;
-    }
-    return step_begin(s - kXDepth) + xops(s);
-  }
-  // instructions issued before step s starts issuing
-  static constexpr int step_begin(int s) {
-    int n = 0;
-    for (int t = 0; t < kRing; ++t) n += wops(t);
-    for (int t = 0; t < kXDepth; ++t) n += xops(t);
-    for (int t = 0; t < s; ++t) n += xops(t + kXDepth) + wops(t + kRing);
-    return n;
-  }
-  // outstanding instructions allowed at the start of step s
-  static constexpr int wait_at(int s) {
-    const int need = w_end(s) > x_end(s) ? w_end(s) : x_end(s);
-    const int v = step_begin(s) - need;
-    return v > 62 ? 62 : v;
-  }
-};
+constexpr int wait_at(int s) {
+  int later = 0;
+  for (int t = s + 1; t < s + kRing && t < NS; ++t) later += kOpsPerStep;
+  return later;
+}
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void dma16(uint32_t lds_dst, uint32_t voff, const u32x4& rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds_dst), "v"(voff), "s"(rsrc)
+               : "m0", "memory");
 }
 
 __device__ __forceinline__ u32x4 asm_load16(uint32_t voff, const u32x4& rsrc) {
@@ -110,227 +93,345 @@ __device__ __forceinline__ u32x4 asm_load16(uint32_t voff, const u32x4& rsrc) {
   return v;
 }
 
-template <int NSTEPS>
-__global__ __launch_bounds__(kThreads, 1) void decode_kernel(ForwardArgs a, int nheads) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
-  using I = Issue<NSTEPS>;
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  float d;
+  // volatile: with a plain asm statement the compiler produced wrong results here
+  asm volatile("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
 
-  // ---- workgroup -> (head, quarter); the 4 quarters of a head share an XCD
+__device__ __forceinline__ u32x4 rsrc_of(const void* p, uint32_t bytes) {
+  const uint64_t base = reinterpret_cast<uint64_t>(p);
+  return u32x4{(uint32_t)base, (uint32_t)(base >> 32), bytes, (uint32_t)kBufferWord3};
+}
+
+// Weight slot: [32 k][128 n] (256-byte rows); 16-byte chunk c of row k sits at
+// chunk c ^ 4*(k mod 4) so a transpose read's 4-row x 16-column blocks hit
+// distinct banks.  Activation slot: [64 tokens][32 k] (64-byte rows); chunk c of
+// token t sits at c ^ ((t / 4) mod 4).
+__device__ __forceinline__ uint32_t wchunk(uint32_t k, uint32_t c) { return c ^ ((k & 3u) << 2); }
+__device__ __forceinline__ uint32_t xchunk(uint32_t t, uint32_t c) { return c ^ ((t >> 2) & 3u); }
+
+template <int NSTEPS>
+__global__ __launch_bounds__(kThreads, 1) void decode_kernel(ForwardArgs a, int nheads, int nsplit) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
+  __shared__ int s_last;
+
+  // ---- unit -> (head, K slice); units of one K slice share XCDs
   const int b = blockIdx.x;
-  int head, q;
-  if ((nheads & 7) == 0) {
+  int head, kq;
+  const int per = 8 / nsplit;  // XCDs per K slice
+  if (nsplit <= 8 && 8 % nsplit == 0 && nheads % per == 0) {
     const int xcd = b & 7, local = b >> 3;
-    q = local & 3;
-    head = (local >> 2) * 8 + xcd;
+    kq = xcd / per;
+    head = (xcd % per) * (nheads / per) + local;
   } else {
-    head = b >> 2;
-    q = b & 3;
+    head = b / nsplit;
+    kq = b % nsplit;
   }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, N = a.N, T = a.T;
-  const int c0 = head * 128 + 16 * q;  // first column of segment 0; segment 1 is c0 + 64
-  const int kbeg = wave * (NSTEPS * kStepK);
+  const int n0 = head * kCols;
+  const int kbeg = kq * (H / nsplit) + wave * (NSTEPS * kStepK);
 
-  auto rsrc_of = [](const void* p, uint32_t bytes) {
-    const uint64_t base = reinterpret_cast<uint64_t>(p);
-    return u32x4{(uint32_t)base, (uint32_t)(base >> 32), bytes, (uint32_t)kBufferWord3};
-  };
   const u32x4 w_rsrc = rsrc_of(a.w, (uint32_t)H * (uint32_t)N * 2u);
   const u32x4 x_rsrc = rsrc_of(a.x, (uint32_t)T * (uint32_t)H * 2u);  // tokens >= T read as 0
   const u32x4 n_rsrc = rsrc_of(a.w_norm, (uint32_t)H * 2u);
-
-  // ---- weight DMA: instruction i of a step covers rows 16i + lane/4 of the slice.
-  // LDS row (64 B) = 4 chunks [seg0 0-7 | seg0 8-15 | seg1 0-7 | seg1 8-15], chunk
-  // index XOR (row/8 mod 4) so the transpose reads of the four k-groups spread
-  // over the banks.
-  const uint32_t lds0 =
+  const uint32_t ring0 =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem + wave * kWaveRing;
-  uint32_t d_voff[2];
+
+  // weight DMA: instruction i covers rows 4i..4i+3; lane -> row 4i + lane/16,
+  // physical chunk lane%16, i.e. logical chunk wchunk(row, lane%16)
+  const uint32_t w_voff = (((uint32_t)kbeg + (lane >> 4)) * N + n0 + 8u * wchunk(lane >> 4, lane & 15)) * 2u;
+  // x DMA: instruction i covers tokens 16i..16i+15; lane -> token 16i + lane/4,
+  // physical chunk lane%4, i.e. logical chunk xchunk(token, lane%4)
+  const uint32_t x_voff = (((uint32_t)(lane >> 2)) * H + kbeg + 8u * xchunk(lane >> 2, lane & 3)) * 2u;
+  auto issue_step = [&](int s) {
+    const uint32_t slot = __builtin_amdgcn_readfirstlane(ring0 + (s % kRing) * kSlot);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t row = 16u * i + (lane >> 2);
-    const uint32_t lc = (uint32_t)(lane & 3) ^ ((row >> 3) & 3u);  // logical chunk held by this lane
-    d_voff[i] = ((uint32_t)(kbeg + row) * N + c0 + 64u * (lc >> 1) + 8u * (lc & 1)) * 2u;
-  }
-  auto dma = [&](int s) {
+    for (int i = 0; i < 8; ++i)
+      dma16(slot + i * 1024, w_voff + ((uint32_t)(s * kStepK + 4 * i)) * (uint32_t)N * 2u, w_rsrc);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (s % kRing) * kStepBytes + i * 1024);
-      const uint32_t voff = d_voff[i] + (uint32_t)(s * kStepK) * (uint32_t)N * 2u;
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(voff),
-                   "s"(w_rsrc)
-                   : "m0", "memory");
-    }
+    for (int i = 0; i < 4; ++i)
+      dma16(slot + kWBytes + i * 1024, x_voff + ((uint32_t)(16 * i) * H + s * kStepK) * 2u, x_rsrc);
   };
-  // ---- B fragments: 16-lane group g reads k rows 8g + 4h + 0..3 of column block cb
+  // norm weight of the lane's k values: k = 16*ks + 8*(lane/32) + 0..7
+  const uint32_t nw_voff = ((uint32_t)kbeg + 8u * (lane >> 5)) * 2u;
+  u32x4 nw[kRing][2];
+  auto issue_nw = [&](int s) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) nw[s % kRing][ks] = asm_load16(nw_voff + (uint32_t)(s * kStepK + 16 * ks) * 2u, n_rsrc);
+  };
+
+  // fragment read offsets within a slot
+  const uint32_t fl = lane & 31, fh = lane >> 5;
+  uint32_t a_off[2][2];  // [token block][k half]
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t t = 32u * tb + fl;
+      a_off[tb][ks] = kWBytes + t * 64u + xchunk(t, 2u * ks + fh) * 16u;
+    }
   const uint32_t tg = lane >> 4, tj = lane & 15;
-  uint32_t t_off[2][2];
+  uint32_t b_off[4];  // [column block]; + ks*16 rows, + 4 rows for the second half
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t row = 8u * tg + 4u * h + (tj >> 2);
-      const uint32_t col = 16u * cb + 4u * (tj & 3);
-      const uint32_t pc = (col >> 3) ^ ((row >> 3) & 3u);
-      t_off[cb][h] = row * 64u + pc * 16u + (col & 7u) * 2u;
-    }
+  for (int cb = 0; cb < 4; ++cb) {
+    const uint32_t krow = 8u * (tg >> 1) + (tj >> 2);
+    const uint32_t col = cb * 32u + 16u * (tg & 1) + 4u * (tj & 3);
+    b_off[cb] = krow * 256u + wchunk(krow, col >> 3) * 16u + (col & 7u) * 2u;
+  }
 
-  // ---- activations: lane -> token tb*16 + lane%16, k = 8 * (lane/16) .. + 7
-  const uint32_t x_voff = ((uint32_t)(lane & 15) * H + kbeg + 8u * (lane >> 4)) * 2u;
-  const uint32_t n_voff = (uint32_t)(kbeg + 8 * (lane >> 4)) * 2u;
-  u32x4 xr[kXDepth][4], nr[kXDepth];
-  auto xload = [&](int s) {
-    const int set = s % kXDepth;
+  f32x16 acc[2][4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-      xr[set][tb] = asm_load16(x_voff + (uint32_t)(tb * 16) * H * 2u + (uint32_t)(s * kStepK) * 2u, x_rsrc);
-    nr[set] = asm_load16(n_voff + (uint32_t)(s * kStepK) * 2u, n_rsrc);
-  };
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tb][cb][r] = 0.f;
+  float ss[2] = {0.f, 0.f};
 
-  f32x4 acc[4][2];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) acc[tb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ss[4] = {0.f, 0.f, 0.f, 0.f};
-
-  // ---- prologue
+  // ---- prologue: kRing steps in flight
 #pragma unroll
   for (int s = 0; s < kRing; ++s)
-    if (s < NSTEPS) dma(s);
-#pragma unroll
-  for (int s = 0; s < kXDepth; ++s)
-    if (s < NSTEPS) xload(s);
+    if (s < NSTEPS) {
+      issue_step(s);
+      issue_nw(s);
+    }
 
   static_for<0, NSTEPS>([&](auto sc) {
     constexpr int s = decltype(sc)::value;
-    constexpr int set = s % kXDepth;
-    vm_wait<I::wait_at(s)>();
-    // make the activation registers of this step depend on the wait
-    asm volatile("" : "+v"(xr[set][0]), "+v"(xr[set][1]), "+v"(xr[set][2]), "+v"(xr[set][3]), "+v"(nr[set]));
-    const uint8_t* slot = smem + wave * kWaveRing + (s % kRing) * kStepBytes;
-    bf16x8 fb[2];
+    constexpr int slot_i = s % kRing;
+    vm_wait<wait_at<NSTEPS>(s)>();
+    asm volatile("" : "+v"(nw[slot_i][0]), "+v"(nw[slot_i][1]));
+    const uint8_t* slot = smem + wave * kWaveRing + slot_i * kSlot;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slot + t_off[cb][0]));
-      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slot + t_off[cb][1]));
-      fb[cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-    float wf[8];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      wf[2 * c] = bf16_lo(nr[set][c]);
-      wf[2 * c + 1] = bf16_hi(nr[set][c]);
-    }
-    bf16x8 fa[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      u32x4 o;
+    for (int ks = 0; ks < 2; ++ks) {
+      // norm weight split into its low and high halves, for the masked dot products
+      uint32_t wlo[4], whi[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float lo = bf16_lo(xr[set][tb][c]), hi = bf16_hi(xr[set][tb][c]);
-        ss[tb] = fmaf(lo, lo, fmaf(hi, hi, ss[tb]));
-        o[c] = pack_bf16x2(lo * wf[2 * c], hi * wf[2 * c + 1]);
+        wlo[c] = nw[slot_i][ks][c] & 0x0000ffffu;
+        whi[c] = nw[slot_i][ks][c] & 0xffff0000u;
       }
-      fa[tb] = __builtin_bit_cast(bf16x8, o);
+      bf16x8 fa[2], fb[4];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(slot + a_off[tb][ks]);
+        u32x4 o;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          ss[tb] = dot2_bf16(raw[c], raw[c], ss[tb]);
+          o[c] = pack_bf16x2(dot2_bf16(raw[c], wlo[c], 0.f), dot2_bf16(raw[c], whi[c], 0.f));
+        }
+        fa[tb] = __builtin_bit_cast(bf16x8, o);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const uint8_t* p = slot + b_off[cb] + ks * 16 * 256;
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 256));
+        fb[cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          acc[tb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tb], fb[cb], acc[tb][cb], 0, 0, 0);
     }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        acc[tb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[tb], fb[cb], acc[tb][cb], 0, 0, 0);
-    // the slot just read is refilled below: its transpose reads must have returned
-    // (they have, since the MFMAs consumed them; the wait makes it explicit)
+    // the slot is refilled next: all its LDS reads must have returned
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if constexpr (s + kXDepth < NSTEPS) xload(s + kXDepth);
-    if constexpr (s + kRing < NSTEPS) dma(s + kRing);
+    if constexpr (s + kRing < NSTEPS) {
+      issue_step(s + kRing);
+      issue_nw(s + kRing);
+    }
   });
 
-  // ---- cross-wave reduction in LDS (fixed order), then the epilogue
-  __syncthreads();  // all rings consumed; the LDS is reused below
-  float* red = reinterpret_cast<float*>(smem);                      // [wave][tb][cb][4][64]
-  float* red_ss = reinterpret_cast<float*>(smem + kWaves * 8192);   // [wave][64 tokens]
+  // ---- the 4 waves' partial sums, added in LDS in a fixed order.
+  // LDS layout red[wave][tb][cb][r/4][lane][r%4]: the 4 accumulator registers
+  // r%4 = 0..3 of a lane are 4 consecutive tokens of one column, kept together so
+  // both the write and the cross-wave read are 16-byte operations.
+  __syncthreads();  // every ring consumed: the LDS is reused below
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
+  for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[(((wave * 4 + tb) * 2 + cb) * 4 + r) * 64 + lane] = acc[tb][cb][r];
+      for (int rq = 0; rq < 4; ++rq)
+        red[(((wave * 2 + tb) * 4 + cb) * 4 + rq) * 64 + lane] =
+            f32x4{acc[tb][cb][4 * rq], acc[tb][cb][4 * rq + 1], acc[tb][cb][4 * rq + 2], acc[tb][cb][4 * rq + 3]};
+  float* red_ss = reinterpret_cast<float*>(smem + kWaves * kTokens * kCols * 4);  // [wave][64]
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    float v = ss[tb];
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    if (lane < 16) red_ss[wave * 64 + tb * 16 + lane] = v;
+  for (int tb = 0; tb < 2; ++tb) {
+    const float v = ss[tb] + __shfl_xor(ss[tb], 32, 64);
+    if (lane < 32) red_ss[wave * kTokens + 32 * tb + lane] = v;
   }
   __syncthreads();
-  if (wave >= 4) return;
-  const int tb = wave;
+  // Unit partial in plan scratch: [16 token quads][128 columns][4 tokens] fp32,
+  // then [64] sums of squares.  Written with agent-scope (sc1) stores, which go to
+  // the device-wide coherence point rather than this XCD's L2; the unit that
+  // arrives last reads them back the same way.  This avoids the full-L2
+  // writeback and invalidate a device-wide fence costs when each XCD has its own
+  // L2.
+  const size_t unit = (size_t)head * nsplit + kq;
+  const uint32_t part_floats = (uint32_t)nheads * nsplit * (kTokens * kCols + kTokens);
+  const u32x4 p_rsrc = rsrc_of(a.partials, part_floats * 4u);
+  const uint32_t part_off = (uint32_t)(unit * (kTokens * kCols)) * 4u;
+  const uint32_t ss_off = (uint32_t)((size_t)nheads * nsplit * (kTokens * kCols) + unit * kTokens) * 4u;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int item = tid + kThreads * it;  // 2048 (token quad, column) cells
+    const int tq = item >> 7, c = item & 127;
+    const int tb = tq >> 3, rq = (tq & 7) >> 1, half = tq & 1;
+    const int cb = c >> 5, ln = half * 32 + (c & 31);
+    f32x4 v = red[(((0 * 2 + tb) * 4 + cb) * 4 + rq) * 64 + ln];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v += red[(((w * 2 + tb) * 4 + cb) * 4 + rq) * 64 + ln];
+    asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen sc1" ::"v"(__builtin_bit_cast(u32x4, v)),
+                 "v"(part_off + (uint32_t)(tq * kCols + c) * 16u), "s"(p_rsrc)
+                 : "memory");
+  }
+  if (tid < kTokens) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += red_ss[w * kTokens + tid];
+    __hip_atomic_store(&a.partials[ss_off / 4 + tid], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // every wave's stores complete before the unit is counted in
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.counters[head], 1u) == (unsigned)(nsplit - 1);
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- last unit of the head: sum the S partials in K-slice order, then epilogue.
+  // Thread -> token quad tq and rotation pairs j0 + 16i (i < 4): every load is
+  // issued before any is used.
+  const int tq = tid >> 4, j0 = tid & 15;
+  const uint32_t head_off = (uint32_t)((size_t)head * nsplit * (kTokens * kCols)) * 4u;
+  const uint32_t head_ss = (uint32_t)((size_t)nheads * nsplit * (kTokens * kCols) + (size_t)head * nsplit * kTokens) * 4u;
+  // per-row / per-column inputs of the epilogue, requested before the partials so
+  // their latency overlaps
   const int Nq = a.Nq, Nkv = a.Nkv;
-  const int col = c0 + (lane & 15);  // segment-0 column; its rotation partner is col + 64
+  const bool rotate = n0 < Nq + Nkv;
+  int32_t prow[4];
+  double frq[4];
+  float bcol[4][2];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) prow[rr] = (rotate && 4 * tq + rr < T) ? a.pos[4 * tq + rr] : 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    frq[i] = a.rev_freq[j0 + 16 * i];
+    bcol[i][0] = a.bias ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[n0 + j0 + 16 * i]) : 0.f;
+    bcol[i][1] = a.bias ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[n0 + j0 + 16 * i + 64]) : 0.f;
+  }
+  u32x4 pv[4][kMaxSplit][2], sv[kMaxSplit];
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    if (s >= nsplit) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // unit block = kTokens * kCols floats = kTokens * kCols / 4 16-byte cells
+        const uint32_t off = head_off + (uint32_t)(s * (kTokens * kCols / 4) + tq * kCols + j0 + 16 * i + 64 * h) * 16u;
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen sc1" : "=v"(pv[i][s][h]) : "v"(off), "s"(p_rsrc) : "memory");
+      }
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen sc1" : "=v"(sv[s]) : "v"(head_ss + (uint32_t)(s * kTokens + 4 * tq) * 4u), "s"(p_rsrc) : "memory");
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  f32x4 y[4][2], sq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) y[i][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    if (s >= nsplit) break;
+    asm volatile("" : "+v"(sv[s]));
+    sq += __builtin_bit_cast(f32x4, sv[s]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        asm volatile("" : "+v"(pv[i][s][h]));
+        y[i][h] += __builtin_bit_cast(f32x4, pv[i][s][h]);
+      }
+  }
   void* out;
-  int width, ocol;
-  if (head * 128 < Nq) {
-    out = a.q; width = Nq; ocol = col;
-  } else if (head * 128 < Nq + Nkv) {
-    out = a.k; width = Nkv; ocol = col - Nq;
+  int width, ocol0;
+  if (n0 < Nq) {
+    out = a.q; width = Nq; ocol0 = n0;
+  } else if (n0 < Nq + Nkv) {
+    out = a.k; width = Nkv; ocol0 = n0 - Nq;
   } else {
-    out = a.v; width = Nkv; ocol = col - Nq - Nkv;
+    out = a.v; width = Nkv; ocol0 = n0 - Nq - Nkv;
   }
-  const bool rotate = head * 128 < Nq + Nkv;
-  float b0 = 0.f, b1 = 0.f;
-  if (a.bias) {
-    b0 = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[col]);
-    b1 = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[col + 64]);
-  }
-  const double rev = a.rev_freq[16 * q + (lane & 15)];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = tb * 16 + (lane >> 4) * 4 + r;
-    float y0 = 0.f, y1 = 0.f, sq = 0.f;
+  for (int rr = 0; rr < 4; ++rr) {
+    const int t = 4 * tq + rr;
+    if (t >= T) break;
+    const float rinv = rsqrtf(sq[rr] / (float)H + a.eps);
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      y0 += red[(((w * 4 + tb) * 2 + 0) * 4 + r) * 64 + lane];
-      y1 += red[(((w * 4 + tb) * 2 + 1) * 4 + r) * 64 + lane];
-      sq += red_ss[w * 64 + t];
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + 16 * i;
+      const float y0r = fmaf(y[i][0][rr], rinv, bcol[i][0]), y1r = fmaf(y[i][1][rr], rinv, bcol[i][1]);
+      float y0 = y0r, y1 = y1r;
+      if (rotate) {
+        float cs, sn;
+        rope_cos_sin(prow[rr], frq[i], cs, sn);
+        const float u = y0, v = y1;
+        y0 = u * cs - v * sn;
+        y1 = v * cs + u * sn;
+      }
+      uint16_t* o = reinterpret_cast<uint16_t*>(out) + (size_t)t * width + ocol0 + j;
+      o[0] = f32_to_bf16(y0);
+      o[64] = f32_to_bf16(y1);
     }
-    if (t >= T) continue;
-    const float rinv = rsqrtf(sq / (float)H + a.eps);
-    y0 = fmaf(y0, rinv, b0);
-    y1 = fmaf(y1, rinv, b1);
-    if (rotate) {
-      float cs, sn;
-      rope_cos_sin(a.pos[t], rev, cs, sn);
-      const float u = y0, v = y1;
-      y0 = u * cs - v * sn;
-      y1 = v * cs + u * sn;
-    }
-    uint16_t* o = reinterpret_cast<uint16_t*>(out) + (size_t)t * width + ocol;
-    o[0] = f32_to_bf16(y0);
-    o[64] = f32_to_bf16(y1);
   }
+  if (tid == 0) a.counters[head] = 0u;  // ready for the next forward on this plan
+}
+
+int pick_split(int nheads, int H) {
+  // aim at one unit per CU (256 CUs) with whole 32-row steps per wave
+  for (int s : {4, 2, 1}) {
+    if (nheads * s > 256) continue;
+    const int rows = H / s;
+    if (H % s == 0 && rows % (kWaves * kStepK) == 0) {
+      const int steps = rows / (kWaves * kStepK);
+      if (steps == 2 || steps == 4 || steps == 8 || steps == 16) return s;
+    }
+  }
+  return 0;
 }
 
 }  // namespace
 
 bool decode_supports(int T, int H, int N, int Nq, int Nkv, int d) {
   return T >= 1 && T <= kTokens && d == 128 && Nq % 128 == 0 && Nkv % 128 == 0 && N % 128 == 0 &&
-         (H == kWaves * kStepK * 16 || H == kWaves * kStepK * 8 || H == kWaves * kStepK * 32);
+         pick_split(N / 128, H) > 0;
+}
+
+size_t decode_scratch_floats(int H, int N) {
+  const int nheads = N / 128;
+  const int s = pick_split(nheads, H);
+  return (size_t)nheads * s * (kTokens * kCols + kTokens);
 }
 
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream) {
   const int nheads = a.N / 128;
-  const int steps = a.H / (kWaves * kStepK);
-  dim3 grid(nheads * 4), block(kThreads);
-  if (steps == 16)
-    decode_kernel<16><<<grid, block, 0, stream>>>(a, nheads);
-  else if (steps == 8)
-    decode_kernel<8><<<grid, block, 0, stream>>>(a, nheads);
-  else if (steps == 32)
-    decode_kernel<32><<<grid, block, 0, stream>>>(a, nheads);
-  else
-    return hipErrorInvalidValue;
+  const int nsplit = pick_split(nheads, a.H);
+  const int steps = a.H / nsplit / (kWaves * kStepK);
+  dim3 grid(nheads * nsplit), block(kThreads);
+  switch (steps) {
+    case 2: decode_kernel<2><<<grid, block, 0, stream>>>(a, nheads, nsplit); break;
+    case 4: decode_kernel<4><<<grid, block, 0, stream>>>(a, nheads, nsplit); break;
+    case 8: decode_kernel<8><<<grid, block, 0, stream>>>(a, nheads, nsplit); break;
+    case 16: decode_kernel<16><<<grid, block, 0, stream>>>(a, nheads, nsplit); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -51,14 +51,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // cos and sin of the rotary angle pos * theta^(-2i/d).  `rev` is that frequency in
 // revolutions per position, theta^(-2i/d) / (2 pi), prepared in fp64 on the host.
-// The product and its reduction to [-1/2, 1/2] revolution are done in fp64, so
-// positions up to 2^31 keep their angle to ~1e-9 rad; the reduced angle is then
-// evaluated by the device math library's sincospi in fp32.
+// The product is formed in fp64 and reduced to the fraction of a turn there, so
+// positions up to 2^31 keep their angle to ~1e-9 rad; the hardware sin/cos
+// (v_sin_f32 / v_cos_f32, which take the angle in turns) evaluate the fraction to
+// ~1.2e-7 absolute.
 __device__ __forceinline__ void rope_cos_sin(int32_t pos, double rev, float& c, float& s) {
-  double turns = (double)pos * rev;
-  double red = turns - rint(turns);            // [-0.5, 0.5] revolution
-  float half_turns = (float)(2.0 * red);       // angle / pi in [-1, 1]
-  sincospif(half_turns, &s, &c);
+  const double turns = (double)pos * rev;
+  const float frac = (float)(turns - floor(turns));  // [0, 1) turn
+  s = __builtin_amdgcn_sinf(frac);
+  c = __builtin_amdgcn_cosf(frac);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

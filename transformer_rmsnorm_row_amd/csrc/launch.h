@@ -32,5 +32,7 @@ hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
 bool prefill_supports(int H, int N, int Nq, int Nkv, int d);
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
 bool decode_supports(int T, int H, int N, int Nq, int Nkv, int d);
+// fp32 elements of plan scratch the decode kernel needs (partials + sums of squares)
+size_t decode_scratch_floats(int H, int N);
 
 }  // namespace qkv

@@ -121,8 +121,18 @@ qkv_status qkv_plan_create(const qkv_plan_desc* desc, qkv_plan* out_plan) {
     return QKV_ERR_HIP;
   }
   const int half = desc->head_dim / 2;
-  if (hipMalloc(&pl->inv_rms, sizeof(float) * (size_t)desc->max_tokens) != hipSuccess ||
-      hipMalloc(&pl->rev_freq, sizeof(double) * (size_t)half) != hipSuccess) {
+  bool ok = hipMalloc(&pl->inv_rms, sizeof(float) * (size_t)desc->max_tokens) == hipSuccess &&
+            hipMalloc(&pl->rev_freq, sizeof(double) * (size_t)half) == hipSuccess;
+  if (ok && pl->decode_ok) {
+    // per-head partial sums of the decode kernel and its arrival counters (zeroed once;
+    // the kernel leaves them at zero after every forward)
+    const size_t nheads = (size_t)pl->N / 128;
+    ok = hipMalloc(&pl->partials, sizeof(float) * qkv::decode_scratch_floats(desc->hidden, pl->N)) == hipSuccess &&
+         hipMalloc(&pl->counters, sizeof(uint32_t) * nheads) == hipSuccess &&
+         hipMemset(pl->counters, 0, sizeof(uint32_t) * nheads) == hipSuccess &&
+         hipDeviceSynchronize() == hipSuccess;
+  }
+  if (!ok) {
     free_scratch(pl);
     delete pl;
     (void)hipGetLastError();
