@@ -185,7 +185,20 @@ def main() -> int:
     ap.add_argument("--workload", default="llama7b_prefill")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (steps times), to scale "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings against a known byte count")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": args.steps}))
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(every token is independent, so the work shards by tokens with no exchange). "

@@ -124,8 +124,6 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tile
   const int wm = wave >> 1, wn = wave & 1;
   const int H = a.H, N = a.N, T = a.T;
 
-  const auto rx = make_rsrc(a.x, (uint32_t)T * (uint32_t)H * 2u);
-  const auto rwn = make_rsrc(a.w_norm, (uint32_t)H * 2u);
 
   // ---- activation slice (registers -> LDS): thread owns chunk kc of rows ar + 32j
   const uint32_t kc = tid & 7, ar = tid >> 3;
@@ -192,12 +190,27 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tile
 
   u32x4 ga[2][8], gw[2];
   // Loads past the end of K read zeros (outside the buffer's range) or rows that
-  // are never used, so the loop body needs no branch.
+  // are never used, so the loop body needs no branch.  Like the weight DMA they are
+  // inline assembly, so that every vector-memory instruction is invisible to the
+  // compiler's wait insertion and the waits below can count them exactly.
+  const uint64_t xbase = reinterpret_cast<uint64_t>(a.x), nbase = reinterpret_cast<uint64_t>(a.w_norm);
+  const u32x4 x_rsrc = {(uint32_t)xbase, (uint32_t)(xbase >> 32), (uint32_t)T * (uint32_t)H * 2u, (uint32_t)kBufferWord3};
+  const u32x4 n_rsrc = {(uint32_t)nbase, (uint32_t)(nbase >> 32), (uint32_t)H * 2u, (uint32_t)kBufferWord3};
+  auto asm_load16 = [](uint32_t voff, const u32x4& rsrc) {
+    u32x4 v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(voff), "s"(rsrc));
+    return v;
+  };
   auto gload_rows = [&](int set, int k0, int j0, int j1) {
 #pragma unroll
-    for (int j = j0; j < j1; ++j) ga[set][j] = buf_load16(rx, a_goff + j * a_gstep + (uint32_t)k0 * 2u);
+    for (int j = j0; j < j1; ++j) ga[set][j] = asm_load16(a_goff + j * a_gstep + (uint32_t)k0 * 2u, x_rsrc);
   };
-  auto gload_w = [&](int set, int k0) { gw[set] = buf_load16(rwn, ((uint32_t)k0 + kc * 8u) * 2u); };
+  auto gload_w = [&](int set, int k0) { gw[set] = asm_load16(((uint32_t)k0 + kc * 8u) * 2u, n_rsrc); };
+  // the activation registers of a set become usable only after an explicit wait
+  auto tie_set = [&](int set) {
+    asm volatile("" : "+v"(ga[set][0]), "+v"(ga[set][1]), "+v"(ga[set][2]), "+v"(ga[set][3]), "+v"(ga[set][4]),
+                 "+v"(ga[set][5]), "+v"(ga[set][6]), "+v"(ga[set][7]), "+v"(gw[set]));
+  };
   // rows j0..j1-1 of a slice: x * norm weight in fp32, rounded once to bf16, into LDS
   auto convert_rows = [&](int set, int stage, int j0, int j1) {
     float wf[8];
@@ -242,6 +255,12 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tile
   // loaded into the freed register set.
   auto body = [&](int kt, int as, int cs, uint32_t bcur, int bnext2) {
     dma_b((kt + 2) * BK, bnext2);
+    // Vector-memory order per slice i: weight DMA of slice i+2 (8), then the
+    // activation loads of slice i+3 (9).  The activation set converted now (slice
+    // kt+1, loaded during slice kt-2) is complete once at most the 17 instructions
+    // of slice kt-1 and the 8 just issued remain.
+    wait_vmcnt<25>();
+    tie_set(cs);
     read_frags(as, bcur, 1, 1);
     mfmas(0);
     convert_rows(cs, as ^ 1, 0, 2);
@@ -266,9 +285,9 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tile
     gload_w(cs, (kt + 3) * BK);
     sched_substep<3, 0, 2, 3>();
     __builtin_amdgcn_sched_barrier(0);
-    // the weight slice read next (issued one slice ago) must have landed: at least
-    // that slice's last 7 activation loads and this slice's 17 loads came after it
-    wait_vmcnt<24>();
+    // the weight slice read next (issued one slice ago) must have landed: that
+    // slice's 9 activation loads and this slice's 17 instructions came after it
+    wait_vmcnt<26>();
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -282,10 +301,14 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tile
   gload_w(0, 0);
   gload_rows(1, BK, 0, 8);
   gload_w(1, BK);
+  wait_vmcnt<9>();  // slice 0 of x (and both weight slices) landed; slice 1 of x may be in flight
+  tie_set(0);
   convert_rows(0, 0, 0, 8);
   gload_rows(0, 2 * BK, 0, 8);
   gload_w(0, 2 * BK);
-  wait_vmcnt<0>();
+  // slice 1 of x (converted in the first slice) must be in before the steady-state
+  // counts apply; only slice 2's 9 loads may remain
+  wait_vmcnt<9>();
   __syncthreads();
 
   uint32_t bcur = kBBase, bn1 = kBBase + kTile, bn2i = 2;
@@ -303,8 +326,16 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(ForwardArgs a, int tile
       bn2i = (bn2i == 2) ? 0 : bn2i + 1;
     }
   }
-  // drain the weight loads that ran past the end before the tile memory is reused
-  wait_vmcnt<0>();
+  // Drain the loads that ran past the end of K before the tile memory is reused.
+  // The activation registers they target are never read again, so the compiler
+  // would hand them to the epilogue: tying them to the wait keeps them reserved
+  // until the late loads have landed.
+  asm volatile("s_waitcnt vmcnt(0)"
+               : "+v"(ga[0][0]), "+v"(ga[0][1]), "+v"(ga[0][2]), "+v"(ga[0][3]), "+v"(ga[0][4]), "+v"(ga[0][5]),
+                 "+v"(ga[0][6]), "+v"(ga[0][7]), "+v"(gw[0]), "+v"(ga[1][0]), "+v"(ga[1][1]), "+v"(ga[1][2]),
+                 "+v"(ga[1][3]), "+v"(ga[1][4]), "+v"(ga[1][5]), "+v"(ga[1][6]), "+v"(ga[1][7]), "+v"(gw[1])
+               :
+               : "memory");
   __syncthreads();
   int32_t* s_pos = reinterpret_cast<int32_t*>(smem + kRowInfo);
   float* s_rinv = reinterpret_cast<float*>(smem + kRowInfo + BM * 4);
