@@ -93,12 +93,6 @@ __device__ __forceinline__ u32x4 asm_load16(uint32_t voff, const u32x4& rsrc) {
   return v;
 }
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  float d;
-  // volatile: with a plain asm statement the compiler produced wrong results here
-  asm volatile("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-  return d;
-}
 
 __device__ __forceinline__ u32x4 rsrc_of(const void* p, uint32_t bytes) {
   const uint64_t base = reinterpret_cast<uint64_t>(p);
