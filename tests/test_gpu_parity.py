@@ -110,6 +110,19 @@ def test_head_shapes(nq, nkv, d, dtype):
     P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL[dtype], wl.name)
 
 
+@pytest.mark.parametrize("hidden", [128, 384, 640, 1152])
+def test_prefill_hidden_sizes(hidden):
+    """K extents that exercise the prefill kernel's loop structure: H = 128 runs only
+    the final group of four 32-wide steps, the others one or more full groups first."""
+    wl = workloads.Workload(11, f"prefill_h{hidden}", 1, 300, hidden, 4, 2, 128, True, 1e4, 1e-6, "bf16",
+                            "per_seq")
+    inp = workloads.make_inputs(wl, seed=hidden)
+    with qkv.Plan.for_workload(wl) as plan:
+        assert plan.variant(wl.tokens) == "prefill"
+        got = run(plan, inp)
+    P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], wl.name)
+
+
 # ---------------------------------------------------------------- inputs the workloads cannot see
 
 def _pin_case(kind, dtype="bf16"):
