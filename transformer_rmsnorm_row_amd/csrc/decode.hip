@@ -19,9 +19,9 @@
 //     weight (32 x 128 bf16) and of x (64 x 32 bf16) global -> LDS with
 //     buffer_load ... lds through a 3-deep ring.  B fragments (weight) come back
 //     with ds_read_b64_tr_b16, A fragments (x) with ds_read_b128; each A element is
-//     multiplied by its norm weight and rounded once to bf16 (normalise-on-load)
-//     with masked v_dot2_f32_bf16, and the squares of x are summed with
-//     v_dot2_f32_bf16 on the raw values for the RMS row reduction.
+//     multiplied by its norm weight in fp32 (exact product) and rounded once to
+//     bf16 (normalise-on-load), and the squares of the raw values are summed for
+//     the RMS row reduction.
 //   * v_mfma_f32_32x32x16_bf16, 2 token blocks x 4 column blocks per 16-wide k.
 //   * The 4 waves add their partial sums in LDS; each unit writes its fp32 partial
 //     (64 x 128) and its partial sums of squares to plan scratch and bumps the
@@ -202,12 +202,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(ForwardArgs a, int 
     const uint8_t* slot = smem + wave * kWaveRing + slot_i * kSlot;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      // norm weight split into its low and high halves, for the masked dot products
-      uint32_t wlo[4], whi[4];
+      float wf[8];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        wlo[c] = nw[slot_i][ks][c] & 0x0000ffffu;
-        whi[c] = nw[slot_i][ks][c] & 0xffff0000u;
+        wf[2 * c] = bf16_lo(nw[slot_i][ks][c]);
+        wf[2 * c + 1] = bf16_hi(nw[slot_i][ks][c]);
       }
       bf16x8 fa[2], fb[4];
 #pragma unroll
@@ -216,8 +215,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(ForwardArgs a, int 
         u32x4 o;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          ss[tb] = dot2_bf16(raw[c], raw[c], ss[tb]);
-          o[c] = pack_bf16x2(dot2_bf16(raw[c], wlo[c], 0.f), dot2_bf16(raw[c], whi[c], 0.f));
+          const float lo = bf16_lo(raw[c]), hi = bf16_hi(raw[c]);
+          ss[tb] = fmaf(lo, lo, fmaf(hi, hi, ss[tb]));
+          o[c] = pack_bf16x2(lo * wf[2 * c], hi * wf[2 * c + 1]);
         }
         fa[tb] = __builtin_bit_cast(bf16x8, o);
       }

@@ -62,14 +62,6 @@ __device__ __forceinline__ void rope_cos_sin(int32_t pos, double rev, float& c, 
   c = __builtin_amdgcn_cosf(frac);
 }
 
-// v_dot2_f32_bf16 (a.lo * b.lo + a.hi * b.hi + c): both products of bf16 values are
-// exact in fp32.  Always through the builtin, never inline assembly: the compiler
-// has to see the instruction to place the wait states it needs next to MFMAs.
-typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a), __builtin_bit_cast(bf16x2_v, b), c, false);
-}
-
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
