@@ -38,28 +38,35 @@ METRIC = "fused RMSNorm+QKV+RoPE tokens/s; TFLOP/s %MFMA peak; decode HBM GB/s %
 COUNTER_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
 
-def kernel_source_digest() -> str:
+# sources each kernel is built from: a counter reading stays valid while these are unchanged
+KERNEL_SOURCES = {
+    "prefill_kernel": ("prefill.hip", "device_common.h", "launch.h"),
+    "decode_kernel": ("decode.hip", "device_common.h", "launch.h"),
+}
+
+
+def kernel_source_digest(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "transformer_rmsnorm_row_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, per_launch_units: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, scaled by
-    the plain-copy calibration it holds; None unless taken on the current kernels."""
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the workload's kernel from the committed rocprofv3
+    counter summary, scaled by the plain-copy calibration it holds; None unless the
+    reading was taken on the kernel's current sources."""
     try:
         with open(COUNTER_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_digest") != kernel_source_digest():
-        return None
     w = rec.get("workloads", {}).get(workload)
-    if not w:
+    if not w or w.get("kernel") not in KERNEL_SOURCES:
+        return None
+    if w.get("kernel_digest") != kernel_source_digest(w["kernel"]):
         return None
     return int(w["hbm_bytes_per_launch"])
 
@@ -82,6 +89,45 @@ def time_forward(plan, bufs, steps: int, warmup: int):
     return wall, start.elapsed_time(end) / 1e3 / steps
 
 
+def time_forward_cold(plan, bufs, calls: int = 20, flush_mib: int = 512):
+    """Per-call times with the last-level cache flushed before each call: a 512 MiB
+    buffer is rewritten between calls so x and W come from HBM.  Returns seconds."""
+    import torch
+    x, w, W, b, pos, q, k, v = bufs
+    scratch = torch.empty(flush_mib << 20, dtype=torch.uint8, device=x.device)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    times = []
+    for i in range(calls):
+        scratch.fill_(i & 0xFF)
+        start.record()
+        plan.forward(x, w, W, b, pos, out=(q, k, v))
+        end.record()
+        end.synchronize()
+        times.append(start.elapsed_time(end) / 1e3)
+    del scratch
+    return sorted(times)
+
+
+def copy_bandwidth(mib: int = 1024, reps: int = 20) -> float:
+    """Achievable HBM bandwidth of a plain device-to-device copy (bytes read + written
+    per second), the practical ceiling the decode step is also reported against."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    seconds = start.elapsed_time(end) / 1e3 / reps
+    return 2.0 * src.numel() / seconds
+
+
 def device_inputs(wl, inp):
     import torch
     dev = "cuda:0"
@@ -96,7 +142,7 @@ def device_inputs(wl, inp):
     return x, w, W, b, pos, q, k, v
 
 
-def decode_leg(qkv, workloads, replays: int = 50, copies: int = 8):
+def decode_leg(qkv, workloads, replays: int = 125, copies: int = 8):
     """Decode step with the weight streamed from HBM: `copies` distinct (x, W) sets
     (8 x 51 MB > the 256 MB last-level cache), visited round-robin.  The forwards are
     captured once in a HIP graph and replayed, so the GPU time per call is not
@@ -146,10 +192,13 @@ def decode_leg(qkv, workloads, replays: int = 50, copies: int = 8):
     plan.close()
     nbytes = wl.algorithmic_bytes()
     gbs = nbytes / per_call / 1e9
+    copy_gbs = copy_bandwidth() / 1e9
     return {
         "workload": wl.name, "tokens": wl.tokens, "variant": variant, "us_per_call": round(per_call * 1e6, 3),
+        "calls_timed": replays * copies,
         "tokens_per_s": round(wl.tokens / per_call, 1), "algorithmic_bytes": nbytes,
         "hbm_GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4),
         "tflops": round(wl.flops() / per_call / 1e12, 2),
         "warm_cache_us_per_call": round(warm * 1e6, 3), "weight_copies_rotated": copies,
         "timing": "HIP graph of one forward per weight copy, replayed",
@@ -172,7 +221,14 @@ def cpu_baseline_leg(wl, inp):
     t0 = time.perf_counter()
     qkv_oracle.qkv_forward(*args)
     dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": round(wl.tokens / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu,
             "sample": f"one full forward of {wl.name} ({wl.tokens} tokens) in fp64, {dt:.2f} s",
             "seconds": round(dt, 3)}
 
@@ -217,18 +273,19 @@ def main() -> int:
     print(f"[bench] {wl.name}: T={wl.tokens} H={wl.hidden} N={wl.n_total} variant={variant} "
           f"steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     wall, kernel_s = time_forward(plan, bufs, args.steps, args.warmup)
+    cold = None
+    if wl.tokens > 256:
+        cold = time_forward_cold(plan, bufs)
     plan.close()
 
     flops = wl.flops()
     nbytes = wl.algorithmic_bytes()
     if wl.tokens <= 256:
         bound, achieved, peak, unit = "hbm", nbytes / kernel_s / 1e9, PEAK_HBM_GBS, "GB/s"
-        units = nbytes
     else:
         peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
         bound, achieved, unit = "mfma", flops / kernel_s / 1e12, "TFLOP/s"
-        units = flops
-    traffic = measured_traffic(wl.name, units)
+    traffic = measured_traffic(wl.name)
     out = {
         "metric": METRIC,
         "value": round(wl.tokens * args.steps / wall, 1),
@@ -252,6 +309,14 @@ def main() -> int:
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_us": round(kernel_s * 1e6, 2), "algorithmic_bytes": nbytes, "flops": flops},
     }
+    if cold:
+        pct = lambda p: cold[min(len(cold) - 1, int(round(p * (len(cold) - 1))))]
+        med = pct(0.5)
+        out["prefill_cold"] = {
+            "calls": len(cold), "median_us": round(med * 1e6, 2), "p10_us": round(pct(0.1) * 1e6, 2),
+            "p90_us": round(pct(0.9) * 1e6, 2), "tflops_median": round(flops / med / 1e12, 2),
+            "frac_median": round(flops / med / 1e12 / peak, 4),
+            "timing": "each call event-bracketed after rewriting a 512 MiB buffer (last-level cache flushed)"}
     if not args.no_decode and wl.name != "gqa_decode":
         print("[bench] decode leg", file=sys.stderr, flush=True)
         out["decode"] = decode_leg(qkv, workloads)
