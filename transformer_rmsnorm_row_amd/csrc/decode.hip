@@ -11,11 +11,14 @@
 // in full 256-byte rows, while the activations stay cheap:
 //
 //   * Work unit = one head (128 output columns, so both members of every rotation
-//     pair are in the unit) x one of S slices of the hidden dimension.  Splitting K
-//     keeps the per-workgroup share of x small (x is read once per unit), so the
-//     CU load path carries mostly weight bytes.  Units of the same K slice are
-//     numbered onto the same XCDs and share their x slice in L2.
-//   * 4 waves per unit split its K slice; each wave streams 32-row steps of the
+//     pair are in the unit) x one of S slices of the hidden dimension, S as large
+//     as keeps one unit per CU (5 for 48 heads: 240 units).  Each CU sustains a
+//     fixed amount of loads in flight, so the weight streams faster the more CUs
+//     take part; splitting K also keeps the per-unit share of x small.  When S
+//     divides 8, units of the same K slice are numbered onto the same XCDs and
+//     share their x slice in L2.
+//   * 4 waves per unit split its K slice (runtime step counts, as even as the 32-row
+//     steps allow); each wave streams 32-row steps of the
 //     weight (32 x 128 bf16) and of x (64 x 32 bf16) global -> LDS with
 //     buffer_load ... lds through a 3-deep ring.  B fragments (weight) come back
 //     with ds_read_b64_tr_b16, A fragments (x) with ds_read_b128; each A element is
@@ -51,31 +54,16 @@ constexpr int kSlot = kWBytes + kXBytes;          // 12 KB
 constexpr int kWaveRing = kRing * kSlot;          // 36 KB
 constexpr int kLds = kWaves * kWaveRing;          // 144 KB
 constexpr int kOpsPerStep = 8 + 4 + 2;            // weight DMA + x DMA + 2 norm-weight loads
-constexpr int kMaxSplit = 4;                      // K slices per head, at most
+constexpr int kMaxSplit = 5;                      // K slices per head, at most
 static_assert(kWaves * kTokens * kCols * 4 + kWaves * kTokens * 4 <= kLds, "wave partials must fit in LDS");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int S, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (S < E) {
-    f(std::integral_constant<int, S>{});
-    static_for<S + 1, E>(f);
-  }
-}
-
 // Vector-memory issue order per wave: steps 0..kRing-1 in the prologue, then
-// step s+kRing right after step s has been consumed.  Every step is kOpsPerStep
-// instructions, so at the start of step s the loads of the (min(kRing, NS-s)-1)
-// later steps may still be outstanding.
-template <int NS>
-constexpr int wait_at(int s) {
-  int later = 0;
-  for (int t = s + 1; t < s + kRing && t < NS; ++t) later += kOpsPerStep;
-  return later;
-}
-
+// step s + kRing right after step s has been consumed, kOpsPerStep instructions
+// each; at the start of step s the loads of the min(kRing, nsteps - s) - 1 later
+// steps may still be outstanding.
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -106,7 +94,9 @@ __device__ __forceinline__ u32x4 rsrc_of(const void* p, uint32_t bytes) {
 __device__ __forceinline__ uint32_t wchunk(uint32_t k, uint32_t c) { return c ^ ((k & 3u) << 2); }
 __device__ __forceinline__ uint32_t xchunk(uint32_t t, uint32_t c) { return c ^ ((t >> 2) & 3u); }
 
-template <int NSTEPS>
+template <int P>
+using Int = std::integral_constant<int, P>;
+
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(ForwardArgs a, int nheads, int nsplit) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
   __shared__ int s_last;
@@ -127,7 +117,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(ForwardArgs a, int 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, N = a.N, T = a.T;
   const int n0 = head * kCols;
-  const int kbeg = kq * (H / nsplit) + wave * (NSTEPS * kStepK);
+  // K slice kq of the head = 32-row steps [gs0, gs1) of the H / 32; its 4 waves split
+  // them as evenly as possible (every wave gets at least one: H / 32 >= 4 nsplit)
+  const int nst = H / kStepK;
+  const int gs0 = nst * kq / nsplit, gs1 = nst * (kq + 1) / nsplit;
+  const int ws0 = gs0 + (gs1 - gs0) * wave / kWaves, ws1 = gs0 + (gs1 - gs0) * (wave + 1) / kWaves;
+  const int nsteps = ws1 - ws0;
+  const int kbeg = ws0 * kStepK;
 
   const u32x4 w_rsrc = rsrc_of(a.w, (uint32_t)H * (uint32_t)N * 2u);
   const u32x4 x_rsrc = rsrc_of(a.x, (uint32_t)T * (uint32_t)H * 2u);  // tokens >= T read as 0
@@ -141,8 +137,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(ForwardArgs a, int 
   // x DMA: instruction i covers tokens 16i..16i+15; lane -> token 16i + lane/4,
   // physical chunk lane%4, i.e. logical chunk xchunk(token, lane%4)
   const uint32_t x_voff = (((uint32_t)(lane >> 2)) * H + kbeg + 8u * xchunk(lane >> 2, lane & 3)) * 2u;
-  auto issue_step = [&](int s) {
-    const uint32_t slot = __builtin_amdgcn_readfirstlane(ring0 + (s % kRing) * kSlot);
+  auto issue_step = [&](int s, int sl) {
+    const uint32_t slot = __builtin_amdgcn_readfirstlane(ring0 + sl * kSlot);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       dma16(slot + i * 1024, w_voff + ((uint32_t)(s * kStepK + 4 * i)) * (uint32_t)N * 2u, w_rsrc);
@@ -153,9 +149,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(ForwardArgs a, int 
   // norm weight of the lane's k values: k = 16*ks + 8*(lane/32) + 0..7
   const uint32_t nw_voff = ((uint32_t)kbeg + 8u * (lane >> 5)) * 2u;
   u32x4 nw[kRing][2];
-  auto issue_nw = [&](int s) {
+  auto issue_nw = [&](int s, int sl) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) nw[s % kRing][ks] = asm_load16(nw_voff + (uint32_t)(s * kStepK + 16 * ks) * 2u, n_rsrc);
+    for (int ks = 0; ks < 2; ++ks) nw[sl][ks] = asm_load16(nw_voff + (uint32_t)(s * kStepK + 16 * ks) * 2u, n_rsrc);
   };
 
   // fragment read offsets within a slot
@@ -186,18 +182,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(ForwardArgs a, int 
       for (int r = 0; r < 16; ++r) acc[tb][cb][r] = 0.f;
   float ss[2] = {0.f, 0.f};
 
-  // ---- prologue: kRing steps in flight
+  // ---- prologue: up to kRing steps in flight
 #pragma unroll
   for (int s = 0; s < kRing; ++s)
-    if (s < NSTEPS) {
-      issue_step(s);
-      issue_nw(s);
+    if (s < nsteps) {
+      issue_step(s, s);
+      issue_nw(s, s);
     }
 
-  static_for<0, NSTEPS>([&](auto sc) {
-    constexpr int s = decltype(sc)::value;
-    constexpr int slot_i = s % kRing;
-    vm_wait<wait_at<NSTEPS>(s)>();
+  // one step s (s % kRing == SL: ring slots and registers are compile-time)
+  auto step = [&](auto SLc, int s) {
+    constexpr int slot_i = decltype(SLc)::value;
+    static_assert(kRing == 3, "the waits below are written out for a 3-deep ring");
+    const int later = min(kRing - 1, nsteps - 1 - s);  // wave-uniform
+    if (later >= 2)
+      vm_wait<2 * kOpsPerStep>();
+    else if (later == 1)
+      vm_wait<kOpsPerStep>();
+    else
+      vm_wait<0>();
     asm volatile("" : "+v"(nw[slot_i][0]), "+v"(nw[slot_i][1]));
     const uint8_t* slot = smem + wave * kWaveRing + slot_i * kSlot;
 #pragma unroll
@@ -236,11 +239,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(ForwardArgs a, int 
     }
     // the slot is refilled next: all its LDS reads must have returned
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if constexpr (s + kRing < NSTEPS) {
-      issue_step(s + kRing);
-      issue_nw(s + kRing);
+    if (s + kRing < nsteps) {
+      issue_step(s + kRing, slot_i);
+      issue_nw(s + kRing, slot_i);
     }
-  });
+  };
+  for (int s = 0; s < nsteps; s += kRing) {
+    step(Int<0>{}, s);
+    if (s + 1 < nsteps) step(Int<1>{}, s + 1);
+    if (s + 2 < nsteps) step(Int<2>{}, s + 2);
+  }
 
   // ---- the 4 waves' partial sums, added in LDS in a fixed order.
   // LDS layout red[wave][tb][cb][r/4][lane][r%4]: the 4 accumulator registers
@@ -389,16 +397,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(ForwardArgs a, int 
 }
 
 int pick_split(int nheads, int H) {
-  // aim at one unit per CU (256 CUs) with whole 32-row steps per wave
-  for (int s : {4, 2, 1}) {
-    if (nheads * s > 256) continue;
-    const int rows = H / s;
-    if (H % s == 0 && rows % (kWaves * kStepK) == 0) {
-      const int steps = rows / (kWaves * kStepK);
-      if (steps == 2 || steps == 4 || steps == 8 || steps == 16) return s;
-    }
-  }
-  return 0;
+  // as many K slices per head as keep one unit per CU (256 CUs), at most kMaxSplit,
+  // with at least one 32-row step per wave
+  if (H % kStepK != 0 || nheads < 1) return 0;
+  const int nst = H / kStepK;
+  int s = min(kMaxSplit, 256 / nheads);
+  s = min(s, nst / kWaves);
+  return s >= 1 ? s : 0;
 }
 
 }  // namespace
@@ -417,16 +422,10 @@ size_t decode_scratch_floats(int H, int N) {
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream) {
   const int nheads = a.N / 128;
   const int nsplit = pick_split(nheads, a.H);
-  const int steps = a.H / nsplit / (kWaves * kStepK);
-  dim3 grid(nheads * nsplit), block(kThreads);
-  switch (steps) {
-    case 2: decode_kernel<2><<<grid, block, 0, stream>>>(a, nheads, nsplit); break;
-    case 4: decode_kernel<4><<<grid, block, 0, stream>>>(a, nheads, nsplit); break;
-    case 8: decode_kernel<8><<<grid, block, 0, stream>>>(a, nheads, nsplit); break;
-    case 16: decode_kernel<16><<<grid, block, 0, stream>>>(a, nheads, nsplit); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (nsplit < 1) return hipErrorInvalidValue;
+  decode_kernel<<<dim3(nheads * nsplit), dim3(kThreads), 0, stream>>>(a, nheads, nsplit);
   return hipGetLastError();
 }
 
 }  // namespace qkv
+
