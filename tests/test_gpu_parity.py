@@ -110,7 +110,7 @@ def test_head_shapes(nq, nkv, d, dtype):
     P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL[dtype], wl.name)
 
 
-@pytest.mark.parametrize("hidden", [128, 384, 640, 1152])
+@pytest.mark.parametrize("hidden", [128, 384, 640, 1152, 5120, 8192])
 def test_prefill_hidden_sizes(hidden):
     """K extents that exercise the prefill kernel's loop structure: H = 128 runs only
     the final group of four 32-wide steps, the others one or more full groups first."""
