@@ -286,14 +286,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   // (t + 1) % 2 held step t - 1, both read in memory phases that ended before this
   // step's first barrier; register set t % 2 was converted in the previous compute
   // phase.  Every wave waits for its own loads of step t + 1 before the barrier that
-  // precedes the other group's reads of it.
-  auto step = [&](auto Pc, int t, auto LastC) {
+  // precedes the other group's reads of it.  Nothing is issued past the end of K:
+  // step K/32 - 2 issues nothing and waits for everything, the last step neither.
+  auto step = [&](auto Pc, int t, auto LastC, auto NoIssueC) {
     constexpr int P = decltype(Pc)::value;
     constexpr bool kLast = decltype(LastC)::value;
+    constexpr bool kNoIssue = decltype(NoIssueC)::value;
     read_frags(P & 1, P);
     if constexpr (!kLast) {
-      issue(t + 2, P & 1, (P + 2) & 3);
-      wait_vmcnt<kIssueOps>();
+      if constexpr (kNoIssue) {
+        wait_vmcnt<0>();
+      } else {
+        issue(t + 2, P & 1, (P + 2) & 3);
+        wait_vmcnt<kIssueOps>();
+      }
       tie_set((P + 1) & 1);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -303,6 +309,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   };
 
   const int nk = H / BK;  // multiple of 4, at least 4
+  // The epilogue's per-row and per-column inputs, requested now so that their latency
+  // hides under the main loop: position of row tid, bias of this lane's two columns,
+  // rotation frequency of its pair.
+  // Range-checked buffer loads need no branch (rows past T read position 0, a plan
+  // without bias reads 0 through an empty range), so nothing waits for them before
+  // their first use in the epilogue.
+  const int hcol = n0 + head * 128;  // first column of this wave's head
+  const int32_t pos_pref =
+      __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.pos, (uint32_t)T * 4u), (int)((uint32_t)(m0 + (tid & (BM - 1))) * 4u), 0, 0);
+  const auto b_rsrc = make_rsrc(a.bias ? a.bias : a.w, a.bias ? (uint32_t)N * 2u : 0u);
+  uint16_t braw[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+    braw[cb] = __builtin_amdgcn_raw_buffer_load_b16(b_rsrc, (int)((uint32_t)(hcol + c0 + cb * 64 + fl) * 2u), 0, 0);
+  const uint64_t rev_bits = __builtin_bit_cast(
+      uint64_t, __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(a.rev_freq, 64u * 8u), (int)((uint32_t)(c0 + fl) * 8u), 0, 0));
   // prologue: steps 0 and 1 issued, step 0 converted into activation slot 0
   issue(0, 0, 0);
   issue(1, 1, 1);
@@ -329,22 +351,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   // phase of waves 0-3 and the other way round
   if (grp == 1) barrier();
 
+  const std::false_type no{};
+  const std::true_type yes{};
   int t = 0;
   for (; t < nk - 4; t += 4) {
-    step(Int<0>{}, t, std::false_type{});
-    step(Int<1>{}, t + 1, std::false_type{});
-    step(Int<2>{}, t + 2, std::false_type{});
-    step(Int<3>{}, t + 3, std::false_type{});
+    step(Int<0>{}, t, no, no);
+    step(Int<1>{}, t + 1, no, no);
+    step(Int<2>{}, t + 2, no, no);
+    step(Int<3>{}, t + 3, no, no);
   }
-  step(Int<0>{}, t, std::false_type{});
-  step(Int<1>{}, t + 1, std::false_type{});
-  step(Int<2>{}, t + 2, std::false_type{});
-  step(Int<3>{}, t + 3, std::true_type{});
+  step(Int<0>{}, t, no, no);
+  step(Int<1>{}, t + 1, no, no);
+  step(Int<2>{}, t + 2, no, yes);
+  step(Int<3>{}, t + 3, yes, no);
   if (grp == 0) barrier();
 
-  // Drain the loads that ran past the end of K before the tile memory is reused.
-  // Tying the staging registers to the wait keeps the compiler from handing them to
-  // the epilogue while late loads may still land in them.
+  // Every load has landed by now (the last two steps issue nothing); the wait, tied
+  // to the staging registers, keeps the compiler from handing those registers to the
+  // epilogue ahead of it.
   asm volatile("s_waitcnt vmcnt(0)"
                : "+v"(gx[0][0]), "+v"(gx[0][1]), "+v"(gw[0]), "+v"(gx[1][0]), "+v"(gx[1][1]), "+v"(gw[1])
                :
@@ -361,15 +385,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
       v += __shfl_xor(v, 2, 64);
       if (kc == 0) s_rinv[arow + 64u * j] = rsqrtf(v / (float)H + a.eps);
     }
-    if (tid < BM) {
-      const int tk = m0 + tid;
-      s_pos[tid] = tk < T ? a.pos[tk] : 0;
-    }
+    if (tid < BM) s_pos[tid] = pos_pref;
   }
   __syncthreads();
 
   // ---- epilogue: scale, bias, rotate, stage as bf16, store
-  const int hcol = n0 + head * 128;  // first column of this wave's head
+  const float bcol[2] = {bf16_to_f32(braw[0]), bf16_to_f32(braw[1])};
+  const double rev = __builtin_bit_cast(double, rev_bits);
   const bool rotate = hcol < a.Nq + a.Nkv;
   void* out;
   uint32_t width, ocol;
@@ -380,11 +402,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   } else {
     out = a.v; width = a.Nkv; ocol = hcol - a.Nq - a.Nkv;
   }
-  float bcol[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-    bcol[cb] = a.bias ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.bias)[hcol + c0 + cb * 64 + fl]) : 0.f;
-  const double rev = a.rev_freq[c0 + fl];
 
   uint8_t* stage = smem + (grp * 2 + head) * kBlockStage;
 #pragma unroll
