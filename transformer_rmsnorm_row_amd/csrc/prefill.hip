@@ -404,30 +404,39 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   }
 
   uint8_t* stage = smem + (grp * 2 + head) * kBlockStage;
+  // one instantiation per case, so the uniform test is not repeated (as a branch)
+  // around every element and independent elements can overlap
+  auto scale_rotate_stage = [&](auto RotC) {
+    constexpr bool kRot = decltype(RotC)::value;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int rbase = rb * 32 + rg * 8 + (int)fh * 4;  // row within the group's 128
-      const f32x4 ri4 = *reinterpret_cast<const f32x4*>(s_rinv + grp * 128 + rbase);
-      const i32x4 p4 = *reinterpret_cast<const i32x4*>(s_pos + grp * 128 + rbase);
+      for (int rg = 0; rg < 4; ++rg) {
+        const int rbase = rb * 32 + rg * 8 + (int)fh * 4;  // row within the group's 128
+        const f32x4 ri4 = *reinterpret_cast<const f32x4*>(s_rinv + grp * 128 + rbase);
+        const i32x4 p4 = *reinterpret_cast<const i32x4*>(s_pos + grp * 128 + rbase);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        float y0 = fmaf(acc[rb][0][rg * 4 + rr], ri4[rr], bcol[0]);
-        float y1 = fmaf(acc[rb][1][rg * 4 + rr], ri4[rr], bcol[1]);
-        if (rotate) {
-          const float tf = turn_fraction(p4[rr], rev);
-          const float c = __builtin_amdgcn_cosf(tf), s = __builtin_amdgcn_sinf(tf);
-          const float u0 = y0, v0 = y1;
-          y0 = u0 * c - v0 * s;
-          y1 = v0 * c + u0 * s;
+        for (int rr = 0; rr < 4; ++rr) {
+          float y0 = fmaf(acc[rb][0][rg * 4 + rr], ri4[rr], bcol[0]);
+          float y1 = fmaf(acc[rb][1][rg * 4 + rr], ri4[rr], bcol[1]);
+          if constexpr (kRot) {
+            const float tf = turn_fraction(p4[rr], rev);
+            const float c = __builtin_amdgcn_cosf(tf), s = __builtin_amdgcn_sinf(tf);
+            const float u0 = y0, v0 = y1;
+            y0 = u0 * c - v0 * s;
+            y1 = v0 * c + u0 * s;
+          }
+          uint16_t* srow = reinterpret_cast<uint16_t*>(stage + (rbase + rr) * kStagePitch);
+          srow[c0 + fl] = f32_to_bf16(y0);
+          srow[c0 + 64 + fl] = f32_to_bf16(y1);
         }
-        uint16_t* srow = reinterpret_cast<uint16_t*>(stage + (rbase + rr) * kStagePitch);
-        srow[c0 + fl] = f32_to_bf16(y0);
-        srow[c0 + 64 + fl] = f32_to_bf16(y1);
       }
     }
-  }
+  };
+  if (rotate)
+    scale_rotate_stage(std::true_type{});
+  else
+    scale_rotate_stage(std::false_type{});
   __syncthreads();
   // wave (grp, slot) stores rows 64 (slot % 2) .. +63 of its (group, head) block
   const auto ro = make_rsrc(out, (uint32_t)T * width * 2u);
