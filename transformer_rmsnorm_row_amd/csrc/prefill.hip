@@ -21,7 +21,7 @@
 //     arithmetic woven in), separated by workgroup barriers, so each SIMD's matrix
 //     pipe is fed by one wave while the other wave reads its next fragments.
 //   * Weight steps [32 k][256 n] go global -> LDS directly (buffer_load ... lds),
-//     issued two steps ahead into a 4-deep ring, 16-byte chunks XOR-swizzled by
+//     issued three steps ahead into a 4-deep ring, 16-byte chunks XOR-swizzled by
 //     k mod 4 so that the MFMA B fragments are read conflict-free with
 //     ds_read_b64_tr_b16 (LDS transpose reads).
 //   * Normalise-on-load: x is loaded into registers two steps ahead, multiplied by
@@ -189,10 +189,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   // buffer's range) or rows that are never used, so the loop needs no branch.
   u32x4 gx[2][2], gw[2];
 
-  // Issue one step's vector-memory work: 2 weight DMA instructions into ring slot
-  // `wstage`, then 2 activation loads and 1 norm-weight load into register set `set`
-  // (5 instructions, always in this order: the waits below count them).
-  auto issue = [&](int t, int set, int wstage) {
+  // Vector-memory work of one step: the weight part is 2 DMA instructions into ring
+  // slot `wstage`, the activation part 2 x loads and 1 norm-weight load into register
+  // set `set`.  The waits below count these instructions.
+  auto issue_w = [&](int t, int wstage) {
     const uint32_t k0 = (uint32_t)t * BK;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -203,11 +203,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(voff), "s"(w_rsrc)
                    : "m0");
     }
+  };
+  auto issue_x = [&](int t, int set) {
+    const uint32_t k0 = (uint32_t)t * BK;
     gx[set][0] = asm_load16(x_voff + k0 * 2u, x_rsrc);
     gx[set][1] = asm_load16(x_voff + x_jstep + k0 * 2u, x_rsrc);
     gw[set] = asm_load16((k0 + kc * 8u) * 2u, n_rsrc);
   };
-  constexpr int kIssueOps = 5;
+  constexpr int kWOps = 2, kXOps = 3;
   // the registers of a set become usable only after an explicit wait
   auto tie_set = [&](int set) { asm volatile("" : "+v"(gx[set][0]), "+v"(gx[set][1]), "+v"(gw[set])); };
 
@@ -236,9 +239,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     }
   };
   // Compute phase: the 16 MFMAs of one step from registers, with the conversion of
-  // register set `set` into activation slot `astage` woven into the first half (one
-  // dword of one row after each MFMA) so that its LDS writes are done well before
-  // the closing barrier.
+  // register set `set` into activation slot `astage` spread over the first 13 (at most
+  // 5 VALU instructions, 20 issue cycles, under each 32-cycle MFMA) and its two LDS
+  // writes placed so that the last MFMAs cover their latency before the barrier.
   auto compute = [&](int set, int astage, bool conv) {
     float wf[8];
     if (conv) {
@@ -263,9 +266,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        if (i == 0) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
-        else if (i < 8) __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-        if (i == 4 || i == 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+        if (i < 13) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+        if (i == 7 || i == 12) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
       }
     }
   };
@@ -275,30 +277,37 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // One step t (t % 4 == P).
-  // Memory phase: read this wave's fragments of step t (ring slots t % 2 and t % 4,
-  // complete since the previous barrier), issue step t + 2 into register set t % 2
-  // and weight slot (t + 2) % 4, and wait until step t + 1 has landed: per wave the
-  // vector-memory order is step after step, 5 instructions each, so "step t + 1
-  // complete" is vmcnt(5) once step t + 2 has been issued.  Compute phase: the MFMAs
-  // of step t, and the conversion of step t + 1 into activation slot (t + 1) % 2.
-  // Slot reuse is safe: weight slot (t + 2) % 4 held step t - 2 and activation slot
-  // (t + 1) % 2 held step t - 1, both read in memory phases that ended before this
-  // step's first barrier; register set t % 2 was converted in the previous compute
-  // phase.  Every wave waits for its own loads of step t + 1 before the barrier that
-  // precedes the other group's reads of it.  Nothing is issued past the end of K:
-  // step K/32 - 2 issues nothing and waits for everything, the last step neither.
-  auto step = [&](auto Pc, int t, auto LastC, auto NoIssueC) {
+  // One step t (t % 4 == P).  Waves 0-3 run the memory phase of step t while waves
+  // 4-7 run the compute phase of step t - 1, and the other way round one phase later.
+  // Memory phase: read this wave's fragments of step t (activation slot t % 2, weight
+  // slot t % 4), issue x(t + 2) into register set t % 2 and W(t + 3) into weight slot
+  // (t + 3) % 4, and wait until x(t + 1) has landed.  Per wave the vector-memory order
+  // is ..., W(t + 1), x(t + 1), W(t + 2), x(t + 2), W(t + 3), so that wait is
+  // vmcnt(7), and it also covers W(t + 1).  Compute phase: the MFMAs of step t and the
+  // conversion of x(t + 1) into activation slot (t + 1) % 2.
+  // Slot reuse is safe: weight slot (t + 3) % 4 held step t - 1, which both groups
+  // read in memory phases that ended before this phase began; activation slot
+  // (t + 1) % 2 held step t - 1 of this group's rows, read in its previous memory
+  // phase; register set t % 2 was converted in the previous compute phase.  Every wave
+  // has its own loads of step t + 1 complete before the barrier that ends its memory
+  // phase t, and the first reads of step t + 1 come after that barrier.
+  // Mode: 0 issue x(t + 2) and W(t + 3); 1 issue x(t + 2) only (t = K/32 - 3);
+  // 2 issue nothing and wait for everything (t = K/32 - 2); 3 the last step.
+  auto step = [&](auto Pc, int t, auto ModeC) {
     constexpr int P = decltype(Pc)::value;
-    constexpr bool kLast = decltype(LastC)::value;
-    constexpr bool kNoIssue = decltype(NoIssueC)::value;
+    constexpr int kMode = decltype(ModeC)::value;
+    constexpr bool kLast = kMode == 3;
     read_frags(P & 1, P);
     if constexpr (!kLast) {
-      if constexpr (kNoIssue) {
-        wait_vmcnt<0>();
+      if constexpr (kMode == 0) {
+        issue_x(t + 2, P & 1);
+        issue_w(t + 3, (P + 3) & 3);
+        wait_vmcnt<2 * kWOps + kXOps>();
+      } else if constexpr (kMode == 1) {
+        issue_x(t + 2, P & 1);
+        wait_vmcnt<kWOps + kXOps>();
       } else {
-        issue(t + 2, P & 1, (P + 2) & 3);
-        wait_vmcnt<kIssueOps>();
+        wait_vmcnt<0>();
       }
       tie_set((P + 1) & 1);
     }
@@ -325,10 +334,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     braw[cb] = __builtin_amdgcn_raw_buffer_load_b16(b_rsrc, (int)((uint32_t)(hcol + c0 + cb * 64 + fl) * 2u), 0, 0);
   const uint64_t rev_bits = __builtin_bit_cast(
       uint64_t, __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(a.rev_freq, 64u * 8u), (int)((uint32_t)(c0 + fl) * 8u), 0, 0));
-  // prologue: steps 0 and 1 issued, step 0 converted into activation slot 0
-  issue(0, 0, 0);
-  issue(1, 1, 1);
-  wait_vmcnt<kIssueOps>();
+  // prologue: W(0..2) and x(0..1) issued, x(0) converted into activation slot 0
+  issue_w(0, 0);
+  issue_x(0, 0);
+  issue_w(1, 1);
+  issue_x(1, 1);
+  issue_w(2, 2);
+  wait_vmcnt<2 * kWOps + kXOps>();
   tie_set(0);
   {
     float wf[8];
@@ -351,22 +363,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   // phase of waves 0-3 and the other way round
   if (grp == 1) barrier();
 
-  const std::false_type no{};
-  const std::true_type yes{};
   int t = 0;
   for (; t < nk - 4; t += 4) {
-    step(Int<0>{}, t, no, no);
-    step(Int<1>{}, t + 1, no, no);
-    step(Int<2>{}, t + 2, no, no);
-    step(Int<3>{}, t + 3, no, no);
+    step(Int<0>{}, t, Int<0>{});
+    step(Int<1>{}, t + 1, Int<0>{});
+    step(Int<2>{}, t + 2, Int<0>{});
+    step(Int<3>{}, t + 3, Int<0>{});
   }
-  step(Int<0>{}, t, no, no);
-  step(Int<1>{}, t + 1, no, no);
-  step(Int<2>{}, t + 2, no, yes);
-  step(Int<3>{}, t + 3, yes, no);
+  step(Int<0>{}, t, Int<0>{});
+  step(Int<1>{}, t + 1, Int<1>{});
+  step(Int<2>{}, t + 2, Int<2>{});
+  step(Int<3>{}, t + 3, Int<3>{});
   if (grp == 0) barrier();
 
-  // Every load has landed by now (the last two steps issue nothing); the wait, tied
+  // Every load has landed by now (step K/32 - 2 waited for all of them); the wait, tied
   // to the staging registers, keeps the compiler from handing those registers to the
   // epilogue ahead of it.
   asm volatile("s_waitcnt vmcnt(0)"
