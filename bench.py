@@ -89,6 +89,29 @@ def time_forward(plan, bufs, steps: int, warmup: int):
     return wall, start.elapsed_time(end) / 1e3 / steps
 
 
+def time_forward_kv_cache(qkv, wl, plan, bufs, steps: int, warmup: int, cap: int = 4096):
+    """Seconds per forward of the key/value-cache form: each sequence owns `cap` cache
+    rows and token t goes to its sequence's first row + pos[t] mod cap."""
+    import torch
+    x, w, W, b, pos, q, k, v = bufs
+    cap = max(cap, wl.seq)  # distinct slots within a sequence
+    seq_of = torch.arange(wl.tokens, device=x.device, dtype=torch.int32) // wl.seq
+    slots = qkv.ring_slots(pos, cap) + seq_of * cap
+    kc = torch.zeros((wl.batch * cap, wl.n_kv), dtype=q.dtype, device=x.device)
+    vc = torch.zeros_like(kc)
+    for _ in range(warmup):
+        plan.forward_kv_cache(x, w, W, b, pos, slots, kc, vc, q=q)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        plan.forward_kv_cache(x, w, W, b, pos, slots, kc, vc, q=q)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps
+
+
 def time_forward_cold(plan, bufs, calls: int = 20, flush_mib: int = 512):
     """Per-call times with the last-level cache flushed before each call: a 512 MiB
     buffer is rewritten between calls so x and W come from HBM.  Returns seconds."""
@@ -188,6 +211,26 @@ def decode_leg(qkv, workloads, replays: int = 125, copies: int = 8):
     end.record()
     torch.cuda.synchronize()
     warm = start.elapsed_time(end) / 1e3 / (replays * copies)
+    # the same step writing K and V into a key/value cache (64 sequences x 4096 rows,
+    # slot = sequence's first row + position mod 4096) instead of dense outputs
+    cap = 4096
+    kc = torch.zeros((wl.tokens * cap, wl.n_kv), dtype=wl.torch_dtype, device="cuda:0")
+    vc = torch.zeros_like(kc)
+    cache_slots = [qkv.ring_slots(s[4], cap) + torch.arange(wl.tokens, device="cuda:0", dtype=torch.int32) * cap
+                   for s in sets]
+    cache_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cache_graph, stream=stream):
+        for s, sl in zip(sets, cache_slots):
+            plan.forward_kv_cache(*s[:5], sl, kc, vc, q=s[5], stream=stream)
+    cache_graph.replay()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(replays):
+        cache_graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    per_call_cache = start.elapsed_time(end) / 1e3 / (replays * copies)
+    del kc, vc
     variant = plan.variant(wl.tokens)
     plan.close()
     nbytes = wl.algorithmic_bytes()
@@ -201,6 +244,8 @@ def decode_leg(qkv, workloads, replays: int = 125, copies: int = 8):
         "copy_GBps": round(copy_gbs, 1), "frac_of_copy": round(gbs / copy_gbs, 4),
         "tflops": round(wl.flops() / per_call / 1e12, 2),
         "warm_cache_us_per_call": round(warm * 1e6, 3), "weight_copies_rotated": copies,
+        "kv_cache_us_per_call": round(per_call_cache * 1e6, 3),
+        "kv_cache_hbm_frac": round(nbytes / per_call_cache / 1e9 / PEAK_HBM_GBS, 4),
         "timing": "HIP graph of one forward per weight copy, replayed",
     }
 
@@ -276,6 +321,7 @@ def main() -> int:
     cold = None
     if wl.tokens > 256:
         cold = time_forward_cold(plan, bufs)
+    cache_s = time_forward_kv_cache(qkv, wl, plan, bufs, args.steps, args.warmup)
     plan.close()
 
     flops = wl.flops()
@@ -309,6 +355,10 @@ def main() -> int:
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_us": round(kernel_s * 1e6, 2), "algorithmic_bytes": nbytes, "flops": flops},
     }
+    out["kv_cache"] = {"us": round(cache_s * 1e6, 2), "tflops": round(flops / cache_s / 1e12, 2),
+                       "time_vs_dense": round(cache_s / kernel_s, 4),
+                       "cache": "K and V rows written to slot = sequence's first row + position mod C "
+                                "of [batch x C, kv_heads*head_dim] caches, C = max(4096, seq_len)"}
     if cold:
         pct = lambda p: cold[min(len(cold) - 1, int(round(p * (len(cold) - 1))))]
         med = pct(0.5)

@@ -112,6 +112,31 @@ qkv_status qkv_forward(qkv_plan plan, int64_t num_tokens,
                        const void* bias, const int32_t* pos,
                        void* q, void* k, void* v, void* stream);
 
+/* The same forward with K and V written into key/value caches instead of dense
+ * buffers: the K row and the V row of token t (nkv*head_dim elements each, dtype of
+ * the plan) go to row slots[t] of k_cache and of v_cache, both dense
+ * [cache_rows, nkv*head_dim]; Q is written densely as in qkv_forward.  This is the
+ * step that follows the chain in generation: the new keys and values appended to the
+ * preallocated, fixed-size cache of the RollingBuffer part of the page
+ * "Liger-Kernel内核级优化：FlashAttention与RollingBuffer详解" (Liger-Kernel
+ * kernel-level optimisation: FlashAttention and RollingBuffer explained), which
+ * reuses the cache circularly: a rolling cache of capacity C for one sequence takes
+ * slots[t] = pos[t] mod C (plus the sequence's first row when several sequences share
+ * one buffer).  Here the caller chooses the slots, so contiguous, paged and rolling
+ * caches all use this one call.
+ * slots: [T] int32, 4-byte aligned.  A token whose slot lies outside [0, cache_rows)
+ * (for instance -1 for padding) writes no K and V; rows that no slot names are left
+ * untouched.  Two tokens of one call must not name the same slot (which of them
+ * lands is then unspecified).  k_cache and v_cache must be 16-byte aligned and
+ * cache_rows >= 1; a cache of 2^31 bytes or more returns QKV_ERR_UNSUPPORTED.
+ * Everything else (other arguments, asynchrony, scratch sharing, errors) is as for
+ * qkv_forward. */
+qkv_status qkv_forward_kv_cache(qkv_plan plan, int64_t num_tokens,
+                                const void* x, const void* w_norm, const void* w_qkv,
+                                const void* bias, const int32_t* pos,
+                                const int32_t* slots, int64_t cache_rows,
+                                void* q, void* k_cache, void* v_cache, void* stream);
+
 /* Queue only the row reduction of the chain: inv_rms[t] = 1/sqrt(mean_k x[t,k]^2 + eps)
  * as fp32 for t < num_tokens, into the caller's device buffer `inv_rms` (4-byte
  * aligned).  Same argument rules, asynchrony and errors as qkv_forward. */

@@ -117,3 +117,29 @@ def qkv_forward_rows(rows, x, w_norm, w_qkv, bias, pos, num_q_heads, num_kv_head
     rows = np.asarray(rows)
     return qkv_forward(np.asarray(x)[rows], w_norm, w_qkv, bias, np.asarray(pos)[rows],
                        num_q_heads, num_kv_heads, head_dim, eps, theta)
+
+
+def kv_cache_write(cache, slots, rows):
+    """Key/value cache after one forward writes its K (or V) rows into it.
+
+    The RollingBuffer part of the page "Liger-Kernel内核级优化：FlashAttention与
+    RollingBuffer详解" (Liger-Kernel kernel-level optimisation: FlashAttention and
+    RollingBuffer explained) keeps keys and values in a buffer allocated once at its
+    full size and writes new rows over old ones in place instead of concatenating.
+    Which row a token lands in is the caller's choice, given as slots[t]: token t's
+    row replaces cache row slots[t]; a slot outside [0, cache rows) writes nothing;
+    every other row keeps its value.  (Reading: the page's ring reuse corresponds to
+    slots[t] = pos[t] mod capacity; the slots themselves are an input here.)
+    Returns a new float64 array; `cache` is not modified.
+    """
+    out = np.array(cache, dtype=np.float64, copy=True)
+    rows = np.asarray(rows, dtype=np.float64)
+    slots = np.asarray(slots)
+    seen = set()
+    for t in range(slots.shape[0]):
+        s = int(slots[t])
+        if 0 <= s < out.shape[0]:
+            assert s not in seen, "two tokens of one forward name the same slot"
+            seen.add(s)
+            out[s] = rows[t]
+    return out

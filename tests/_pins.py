@@ -307,4 +307,53 @@ def pin_chain_against_complex(o):
             _close(g_, r_, 1e-10, f"chain {name} vs complex formulation (T={T},H={H},d={d})")
 
 
+def pin_kv_cache_rolling_window(o):
+    """A rolling cache of capacity C fed one token at a time at slot pos mod C always
+    holds, read from the oldest position to the newest, exactly the last C rows: the
+    sliding window that keeps the newest tokens and drops the oldest, as the page's
+    RollingBuffer part describes.  The window here is kept by plain list slicing."""
+    rng = _rng(41)
+    C, T, w = 5, 13, 3
+    rows = rng.standard_normal((T, w))
+    cache = np.full((C, w), 7.0)
+    window = []
+    for p in range(T):
+        cache = o.kv_cache_write(cache, np.array([p % C]), rows[p:p + 1])
+        window = (window + [rows[p]])[-C:]
+        oldest = max(0, p - C + 1)
+        view = np.stack([cache[q % C] for q in range(oldest, p + 1)])
+        _close(view, np.stack(window), 0.0, "rolling view")
+
+
+def pin_kv_cache_chunks_equal_single_steps(o):
+    """Writing a chunk of up to C tokens in one call (distinct slots) leaves the same
+    cache as writing them one by one."""
+    rng = _rng(42)
+    C, T, w = 8, 21, 4
+    rows = rng.standard_normal((T, w))
+    one = np.zeros((C, w))
+    for p in range(T):
+        one = o.kv_cache_write(one, np.array([p % C]), rows[p:p + 1])
+    chunked = np.zeros((C, w))
+    for start in range(0, T, 6):
+        pos = np.arange(start, min(T, start + 6))
+        chunked = o.kv_cache_write(chunked, pos % C, rows[pos])
+    _close(chunked, one, 0.0, "chunked cache")
+
+
+def pin_kv_cache_untouched_and_dropped(o):
+    """Rows no slot names keep their values; slots -1 and past the end write nothing;
+    a named row holds exactly the token's row."""
+    rng = _rng(43)
+    R, w = 6, 3
+    cache = rng.standard_normal((R, w))
+    rows = rng.standard_normal((5, w))
+    slots = np.array([4, -1, 0, R, R + 3])
+    out = o.kv_cache_write(cache, slots, rows)
+    expect = cache.copy()
+    expect[4] = rows[0]
+    expect[0] = rows[2]
+    _close(out, expect, 0.0, "cache rows")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -86,6 +86,7 @@ def test_null_pointers_rejected():
     assert lib.qkv_plan_create(ctypes.byref(d), None) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_forward(None, 4, *([None] * 8), None) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_rms_inv(None, 4, None, None, None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_forward_kv_cache(None, 4, *([None] * 6), 16, None, None, None, None) == qkv.QKV_ERR_INVALID_ARG
     v = ctypes.c_int32()
     assert lib.qkv_plan_variant(None, 4, ctypes.byref(v)) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_plan_destroy(None) == qkv.QKV_OK
@@ -96,6 +97,8 @@ def test_unknown_handle_rejected():
     fake = ctypes.create_string_buffer(256)
     assert lib.qkv_plan_destroy(ctypes.cast(fake, ctypes.c_void_p)) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_forward(ctypes.cast(fake, ctypes.c_void_p), 1, *([None] * 8), None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_forward_kv_cache(ctypes.cast(fake, ctypes.c_void_p), 1, *([None] * 6), 16,
+                                    None, None, None, None) == qkv.QKV_ERR_INVALID_ARG
 
 
 def test_valid_descriptor_without_gpu():
@@ -109,3 +112,15 @@ def test_valid_descriptor_without_gpu():
     else:
         assert st == qkv.QKV_ERR_HIP
         assert h.value is None
+
+
+def test_ring_slots_helper():
+    """Rolling-cache rows: position p of a cache of capacity C starting at row b is
+    row b + p mod C (negative positions wrap the same way)."""
+    import torch
+    pos = torch.tensor([0, 1, 4, 5, 9, 10, -1], dtype=torch.int32)
+    got = qkv.ring_slots(pos, 5, first_row=100)
+    assert got.dtype == torch.int32
+    assert got.tolist() == [100, 101, 104, 100, 104, 100, 104]
+    with pytest.raises(ValueError):
+        qkv.ring_slots(pos, 0)

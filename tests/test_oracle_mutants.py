@@ -35,6 +35,11 @@ MUTANTS = {
     "v_rotated": [("v = y[:, n_q + n_kv:].copy()", "v = rope(y[:, n_q + n_kv:], pos, head_dim, theta)")],
     "k_not_rotated": [("k = rope(y[:, n_q:n_q + n_kv], pos, head_dim, theta)", "k = y[:, n_q:n_q + n_kv].copy()")],
     "q_not_rotated": [("q = rope(y[:, :n_q], pos, head_dim, theta)", "q = y[:, :n_q].copy()")],
+    "cache_slot_wraps": [("if 0 <= s < out.shape[0]:", "s = s % out.shape[0]\n        if True:")],
+    "cache_slot_off_by_one": [("out[s] = rows[t]", "out[(s + 1) % out.shape[0]] = rows[t]")],
+    "cache_cleared": [("out = np.array(cache, dtype=np.float64, copy=True)",
+                       "out = np.zeros_like(np.asarray(cache, dtype=np.float64))")],
+    "cache_token_order_reversed": [("out[s] = rows[t]", "out[s] = rows[slots.shape[0] - 1 - t]")],
     "k_v_swapped": [("k = rope(y[:, n_q:n_q + n_kv], pos, head_dim, theta)",
                      "k = rope(y[:, n_q + n_kv:], pos, head_dim, theta)"),
                     ("v = y[:, n_q + n_kv:].copy()", "v = y[:, n_q:n_q + n_kv].copy()")],

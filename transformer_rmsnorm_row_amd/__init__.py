@@ -25,6 +25,8 @@ _vp = ctypes.c_void_p
 EXPORTS = {
     "qkv_plan_create": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
     "qkv_forward": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "qkv_forward_kv_cache": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
+                                            _vp, _vp, _vp, _vp]),
     "qkv_rms_inv": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp]),
     "qkv_plan_variant": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)]),
     "qkv_plan_destroy": (ctypes.c_int, [_vp]),
@@ -98,6 +100,14 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 def _stream_handle(stream: Optional[torch.cuda.Stream]) -> int:
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+def ring_slots(pos: torch.Tensor, capacity: int, first_row: int = 0) -> torch.Tensor:
+    """Cache rows of a rolling (circular) key/value cache of ``capacity`` rows that
+    starts at row ``first_row``: position p goes to ``first_row + p mod capacity``."""
+    if capacity < 1:
+        raise ValueError("capacity must be at least 1")
+    return (first_row + torch.remainder(pos.to(torch.int64), capacity)).to(torch.int32)
 
 
 class Plan:
@@ -181,6 +191,34 @@ class Plan:
                                    _ptr(q), _ptr(k), _ptr(v), _stream_handle(stream))
         _check(st, "qkv_forward")
         return q, k, v
+
+    def forward_kv_cache(self, x: torch.Tensor, w_norm: torch.Tensor, w_qkv: torch.Tensor,
+                         bias: Optional[torch.Tensor], pos: torch.Tensor, slots: torch.Tensor,
+                         k_cache: torch.Tensor, v_cache: torch.Tensor, q: Optional[torch.Tensor] = None,
+                         stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """One forward whose K and V rows land in rows ``slots[t]`` of the caches
+        (``[rows, nkv*head_dim]``, updated in place); returns Q.  Slots outside the
+        cache write nothing."""
+        T = x.shape[0]
+        H, N = self.hidden, self.n_q + 2 * self.n_kv
+        self._check_tensor(x, "x", (T, H), self.dtype)
+        self._check_tensor(w_norm, "w_norm", (H,), self.dtype)
+        self._check_tensor(w_qkv, "w_qkv", (H, N), self.dtype)
+        if bias is not None:
+            self._check_tensor(bias, "bias", (N,), self.dtype)
+        self._check_tensor(pos, "pos", (T,), torch.int32)
+        self._check_tensor(slots, "slots", (T,), torch.int32)
+        rows = k_cache.shape[0] if k_cache.dim() == 2 else -1
+        self._check_tensor(k_cache, "k_cache", (rows, self.n_kv), self.dtype)
+        self._check_tensor(v_cache, "v_cache", (rows, self.n_kv), self.dtype)
+        if q is None:
+            q = torch.empty((T, self.n_q), dtype=self.dtype, device=x.device)
+        self._check_tensor(q, "q", (T, self.n_q), self.dtype)
+        st = self._lib.qkv_forward_kv_cache(self.handle, T, _ptr(x), _ptr(w_norm), _ptr(w_qkv), _ptr(bias),
+                                            _ptr(pos), _ptr(slots), rows, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                            _stream_handle(stream))
+        _check(st, "qkv_forward_kv_cache")
+        return q
 
     def rms_inv(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:

@@ -371,10 +371,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(ForwardArgs a, int 
   } else {
     out = a.v; width = Nkv; ocol0 = n0 - Nq - Nkv;
   }
+  const bool to_cache = a.slots != nullptr && n0 >= Nq;  // K/V rows go to cache slots
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int t = 4 * tq + rr;
     if (t >= T) break;
+    int row = t;
+    if (to_cache) {
+      row = a.slots[t];
+      if (row < 0 || row >= a.cache_rows) continue;
+    }
     const float rinv = rsqrtf(sq[rr] / (float)H + a.eps);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -388,7 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(ForwardArgs a, int 
         y0 = u * cs - v * sn;
         y1 = v * cs + u * sn;
       }
-      uint16_t* o = reinterpret_cast<uint16_t*>(out) + (size_t)t * width + ocol0 + j;
+      uint16_t* o = reinterpret_cast<uint16_t*>(out) + (size_t)row * width + ocol0 + j;
       o[0] = f32_to_bf16(y0);
       o[64] = f32_to_bf16(y1);
     }

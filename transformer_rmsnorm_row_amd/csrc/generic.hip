@@ -119,6 +119,7 @@ __global__ __launch_bounds__(256) void generic_kernel(ForwardArgs a) {
   } else {
     out = a.v; width = a.Nkv; oc = c - a.Nq - a.Nkv;
   }
+  const bool to_cache = a.slots != nullptr && c >= a.Nq;  // K/V rows go to cache slots
   const double rev = a.rev_freq[i];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -133,8 +134,13 @@ __global__ __launch_bounds__(256) void generic_kernel(ForwardArgs a) {
       y0 = r0;
       y1 = r1;
     }
-    store_elem<BF16>(out, (size_t)t * width + oc, y0);
-    store_elem<BF16>(out, (size_t)t * width + oc + half, y1);
+    int row = t;
+    if (to_cache) {
+      row = a.slots[t];
+      if (row < 0 || row >= a.cache_rows) continue;
+    }
+    store_elem<BF16>(out, (size_t)row * width + oc, y0);
+    store_elem<BF16>(out, (size_t)row * width + oc + half, y1);
   }
 }
 

@@ -20,6 +20,11 @@ struct ForwardArgs {
   const double* rev_freq;  // [head_dim/2] rotary frequencies, revolutions per position
   float* partials;         // decode scratch
   uint32_t* counters;      // decode scratch
+  // KV-cache form: when non-null, K and V of token t go to row slots[t] of k and v,
+  // which then hold cache_rows rows; tokens whose slot is outside [0, cache_rows)
+  // write no K/V.  Q stays dense.
+  const int32_t* slots;
+  int cache_rows;
   int T, H, N, Nq, Nkv, d;
   float eps;
   bool bf16;

@@ -58,8 +58,8 @@ constexpr int kWBase = 0;
 constexpr int kABase = kWStages * kStep;
 constexpr int kStagePitch = 272;                    // 128 bf16 + 16 B pad per staged output row
 constexpr int kBlockStage = 128 * kStagePitch;      // one group's 128 rows x one head
-constexpr int kRowInfo = 4 * kBlockStage;           // per-row pos and 1/rms after the staging area
-constexpr int kLds = kRowInfo + BM * 8;
+constexpr int kRowInfo = 4 * kBlockStage;           // per-row pos, 1/rms, cache slot after the staging area
+constexpr int kLds = kRowInfo + BM * 12;
 static_assert(kABase + kAStages * kStep <= kLds, "loop rings must fit");
 static_assert(kLds <= 160 * 1024, "LDS budget of one workgroup");
 constexpr int kGroupM = 4;
@@ -319,14 +319,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
 
   const int nk = H / BK;  // multiple of 4, at least 4
   // The epilogue's per-row and per-column inputs, requested now so that their latency
-  // hides under the main loop: position of row tid, bias of this lane's two columns,
-  // rotation frequency of its pair.
+  // hides under the main loop: position (and cache slot) of row tid, bias of this
+  // lane's two columns, rotation frequency of its pair.
   // Range-checked buffer loads need no branch (rows past T read position 0, a plan
   // without bias reads 0 through an empty range), so nothing waits for them before
   // their first use in the epilogue.
   const int hcol = n0 + head * 128;  // first column of this wave's head
   const int32_t pos_pref =
       __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.pos, (uint32_t)T * 4u), (int)((uint32_t)(m0 + (tid & (BM - 1))) * 4u), 0, 0);
+  const int32_t slot_pref = __builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(a.slots ? a.slots : a.pos, a.slots ? (uint32_t)T * 4u : 0u), (int)((uint32_t)(m0 + (tid & (BM - 1))) * 4u), 0, 0);
   const auto b_rsrc = make_rsrc(a.bias ? a.bias : a.w, a.bias ? (uint32_t)N * 2u : 0u);
   uint16_t braw[2];
 #pragma unroll
@@ -386,6 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   __syncthreads();
   int32_t* s_pos = reinterpret_cast<int32_t*>(smem + kRowInfo);
   float* s_rinv = reinterpret_cast<float*>(smem + kRowInfo + BM * 4);
+  int32_t* s_slot = reinterpret_cast<int32_t*>(smem + kRowInfo + BM * 8);
   {
     // the four lanes holding the chunks of a row are adjacent (kc = lane % 4)
 #pragma unroll
@@ -395,7 +398,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
       v += __shfl_xor(v, 2, 64);
       if (kc == 0) s_rinv[arow + 64u * j] = rsqrtf(v / (float)H + a.eps);
     }
-    if (tid < BM) s_pos[tid] = pos_pref;
+    if (tid < BM) {
+      s_pos[tid] = pos_pref;
+      s_slot[tid] = m0 + tid < T ? slot_pref : -1;  // rows past T write nothing
+    }
   }
   __syncthreads();
 
@@ -448,15 +454,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   else
     scale_rotate_stage(std::false_type{});
   __syncthreads();
-  // wave (grp, slot) stores rows 64 (slot % 2) .. +63 of its (group, head) block
-  const auto ro = make_rsrc(out, (uint32_t)T * width * 2u);
+  // wave (grp, slot) stores rows 64 (slot % 2) .. +63 of its (group, head) block.
+  // K and V rows go to their cache slots when the forward has them; a row index of
+  // out_rows or more lies past the buffer's range, so that store is dropped.
+  const bool to_cache = a.slots != nullptr && hcol >= a.Nq;
+  const uint32_t out_rows = to_cache ? (uint32_t)a.cache_rows : (uint32_t)T;
+  const auto ro = make_rsrc(out, out_rows * width * 2u);
   const uint32_t ch = lane & 15;
 #pragma unroll 4
   for (int it = 0; it < 16; ++it) {
     const uint32_t row = 64u * (slot & 1) + 4u * it + (lane >> 4);
     const u32x4 v = lds_read16(stage, row * kStagePitch + ch * 16u);
-    const uint32_t grow = (uint32_t)(m0 + 128 * grp) + row;
-    buf_store16(v, ro, (grow * width + ocol + ch * 8u) * 2u);
+    uint32_t orow = (uint32_t)(m0 + 128 * grp) + row;
+    if (to_cache) {
+      const int32_t sr = s_slot[128 * grp + row];
+      orow = sr >= 0 && sr < a.cache_rows ? (uint32_t)sr : out_rows;
+    }
+    buf_store16(v, ro, (orow * width + ocol + ch * 8u) * 2u);
   }
 }
 

@@ -94,6 +94,59 @@ int choose_variant(const Plan* pl, int64_t T) {
   return QKV_VARIANT_GENERIC;
 }
 
+// Validation shared by both forward entry points, then the launch of the variant.
+// k and v are dense [T, Nkv] outputs, or caches of cache_rows rows when slots is set.
+qkv_status launch_forward(Plan* pl, int64_t num_tokens, const void* x, const void* w_norm, const void* w_qkv,
+                          const void* bias, const int32_t* pos, void* q, void* k, void* v, const int32_t* slots,
+                          int cache_rows, void* stream) {
+  if (!x || !w_norm || !w_qkv || !pos || !q) return QKV_ERR_INVALID_ARG;
+  if ((bias != nullptr) != (pl->desc.has_bias == 1)) return QKV_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w_norm, 16) || !aligned(w_qkv, 16) || !aligned(q, 16) || !aligned(pos, 4) ||
+      (bias && !aligned(bias, 16)))
+    return QKV_ERR_INVALID_ARG;
+  qkv_status st = check_device(pl);
+  if (st != QKV_OK) return st;
+
+  qkv::ForwardArgs a{};
+  a.x = x;
+  a.w_norm = w_norm;
+  a.w = w_qkv;
+  a.bias = bias;
+  a.pos = pos;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.inv_rms = pl->inv_rms;
+  a.rev_freq = pl->rev_freq;
+  a.partials = pl->partials;
+  a.counters = pl->counters;
+  a.slots = slots;
+  a.cache_rows = slots ? cache_rows : (int)num_tokens;
+  a.T = (int)num_tokens;
+  a.H = pl->desc.hidden;
+  a.N = pl->N;
+  a.Nq = pl->Nq;
+  a.Nkv = pl->Nkv;
+  a.d = pl->desc.head_dim;
+  a.eps = (float)pl->desc.eps;
+  a.bf16 = pl->bf16;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  hipError_t e;
+  switch (choose_variant(pl, num_tokens)) {
+    case QKV_VARIANT_PREFILL:
+      e = qkv::launch_prefill(a, s);
+      break;
+    case QKV_VARIANT_DECODE:
+      e = qkv::launch_decode(a, s);
+      break;
+    default:
+      e = qkv::launch_generic(a, s);
+      break;
+  }
+  return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,50 +224,23 @@ qkv_status qkv_forward(qkv_plan plan, int64_t num_tokens, const void* x, const v
   if (!pl) return QKV_ERR_INVALID_ARG;
   if (num_tokens == 0) return QKV_OK;
   if (num_tokens < 0 || num_tokens > pl->desc.max_tokens) return QKV_ERR_INVALID_ARG;
-  if (!x || !w_norm || !w_qkv || !pos || !q || !k || !v) return QKV_ERR_INVALID_ARG;
-  if ((bias != nullptr) != (pl->desc.has_bias == 1)) return QKV_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(w_norm, 16) || !aligned(w_qkv, 16) || !aligned(q, 16) || !aligned(k, 16) ||
-      !aligned(v, 16) || !aligned(pos, 4) || (bias && !aligned(bias, 16)))
-    return QKV_ERR_INVALID_ARG;
-  qkv_status st = check_device(pl);
-  if (st != QKV_OK) return st;
+  if (!k || !v || !aligned(k, 16) || !aligned(v, 16)) return QKV_ERR_INVALID_ARG;
+  return launch_forward(pl, num_tokens, x, w_norm, w_qkv, bias, pos, q, k, v, nullptr, 0, stream);
+}
 
-  qkv::ForwardArgs a{};
-  a.x = x;
-  a.w_norm = w_norm;
-  a.w = w_qkv;
-  a.bias = bias;
-  a.pos = pos;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.inv_rms = pl->inv_rms;
-  a.rev_freq = pl->rev_freq;
-  a.partials = pl->partials;
-  a.counters = pl->counters;
-  a.T = (int)num_tokens;
-  a.H = pl->desc.hidden;
-  a.N = pl->N;
-  a.Nq = pl->Nq;
-  a.Nkv = pl->Nkv;
-  a.d = pl->desc.head_dim;
-  a.eps = (float)pl->desc.eps;
-  a.bf16 = pl->bf16;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-
-  hipError_t e;
-  switch (choose_variant(pl, num_tokens)) {
-    case QKV_VARIANT_PREFILL:
-      e = qkv::launch_prefill(a, s);
-      break;
-    case QKV_VARIANT_DECODE:
-      e = qkv::launch_decode(a, s);
-      break;
-    default:
-      e = qkv::launch_generic(a, s);
-      break;
-  }
-  return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
+qkv_status qkv_forward_kv_cache(qkv_plan plan, int64_t num_tokens, const void* x, const void* w_norm,
+                                const void* w_qkv, const void* bias, const int32_t* pos, const int32_t* slots,
+                                int64_t cache_rows, void* q, void* k_cache, void* v_cache, void* stream) {
+  Plan* pl = as_plan(plan);
+  if (!pl) return QKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return QKV_OK;
+  if (num_tokens < 0 || num_tokens > pl->desc.max_tokens) return QKV_ERR_INVALID_ARG;
+  if (!slots || !aligned(slots, 4) || cache_rows < 1) return QKV_ERR_INVALID_ARG;
+  if (!k_cache || !v_cache || !aligned(k_cache, 16) || !aligned(v_cache, 16)) return QKV_ERR_INVALID_ARG;
+  const int64_t elem = pl->bf16 ? 2 : 4;
+  if (cache_rows >= kMaxBytes / ((int64_t)pl->Nkv * elem)) return QKV_ERR_UNSUPPORTED;
+  return launch_forward(pl, num_tokens, x, w_norm, w_qkv, bias, pos, q, k_cache, v_cache, slots, (int)cache_rows,
+                        stream);
 }
 
 qkv_status qkv_rms_inv(qkv_plan plan, int64_t num_tokens, const void* x, float* inv_rms, void* stream) {
