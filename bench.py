@@ -250,6 +250,32 @@ def decode_leg(qkv, workloads, replays: int = 125, copies: int = 8):
     }
 
 
+def swiglu_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
+    """The gated-MLP forward (RMSNorm, gate|up GEMM, SiLU(g) * u) on the Llama-7B MLP
+    shape, timed with HIP events on the current stream."""
+    import torch
+    wl = workloads.MLP_WORKLOADS["llama7b_mlp"]
+    inp = workloads.make_mlp_inputs(wl)
+    x, w, W = (inp[k].to("cuda:0") for k in ("x", "w_norm", "w_gate_up"))
+    out = qkv.swiglu_forward(x, w, W, wl.eps)
+    for _ in range(warmup):
+        qkv.swiglu_forward(x, w, W, wl.eps, out=out)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        qkv.swiglu_forward(x, w, W, wl.eps, out=out)
+    end.record()
+    torch.cuda.synchronize()
+    sec = start.elapsed_time(end) / 1e3 / steps
+    tf = wl.flops() / sec / 1e12
+    return {"workload": wl.name, "tokens": wl.tokens, "hidden": wl.hidden, "intermediate": wl.intermediate,
+            "us": round(sec * 1e6, 2), "tokens_per_s": round(wl.tokens / sec, 1), "tflops": round(tf, 2),
+            "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": wl.flops(),
+            "algorithmic_bytes": wl.algorithmic_bytes()}
+
+
 def cpu_baseline_leg(wl, inp):
     """The fp64 oracle, as it stands, on the host cores: one full forward."""
     import numpy as np
@@ -370,6 +396,9 @@ def main() -> int:
     if not args.no_decode and wl.name != "gqa_decode":
         print("[bench] decode leg", file=sys.stderr, flush=True)
         out["decode"] = decode_leg(qkv, workloads)
+    if not args.no_decode and wl.name != "gqa_decode":
+        print("[bench] gated-MLP leg", file=sys.stderr, flush=True)
+        out["swiglu"] = swiglu_leg(qkv, workloads)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline leg", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_leg(wl, inp)

@@ -143,6 +143,32 @@ qkv_status qkv_forward_kv_cache(qkv_plan plan, int64_t num_tokens,
 qkv_status qkv_rms_inv(qkv_plan plan, int64_t num_tokens, const void* x,
                        float* inv_rms, void* stream);
 
+/* Gated MLP of the same decoder layer on the same normalise-on-load kernel:
+ *
+ *     r[t]     = 1 / sqrt( (1/H) * sum_k x[t,k]^2 + eps )
+ *     a[t,k]   = x[t,k] * r[t] * w_norm[k]
+ *     g, u     = a @ W_gate, a @ W_up          (W_gate_up = [W_gate | W_up], [H, 2I])
+ *     out[t,j] = SiLU(g[t,j]) * u[t,j],  SiLU(z) = z / (1 + exp(-z))
+ *
+ * The fused linear SwiGLU of the operator-fusion section ("算子融合") of the page
+ * "Liger-Kernel核心技术：RollingBuffer与融合算子详解" (Liger-Kernel core techniques:
+ * RollingBuffer and fused operators explained): both products of one input against
+ * the gate and up weights, the SiLU and the elementwise product done in registers,
+ * only the result written; preceded here by the layer's RMSNorm, exactly as in
+ * qkv_forward.  No bias.
+ * Layouts (dense, row-major): x [T, H], w_norm [H], w_gate_up [H, 2I] with the gate
+ * columns first, out [T, I]; all 16-byte aligned.  Stateless: no plan, nothing
+ * allocated, asynchronous on `stream`; runs on the current device.
+ * bf16 only (dtype = QKV_BF16), H and I multiples of 128, and each of x, w_gate_up
+ * and out under 2^31 bytes; other shapes or QKV_F32 return QKV_ERR_UNSUPPORTED.
+ * num_tokens == 0 is a no-op; negative sizes, a bad dtype code, eps negative or not
+ * finite, null or misaligned pointers return QKV_ERR_INVALID_ARG before any HIP call;
+ * a failed launch returns QKV_ERR_HIP. */
+qkv_status qkv_swiglu_forward(int64_t num_tokens, int32_t hidden, int32_t intermediate,
+                              int32_t dtype, double eps,
+                              const void* x, const void* w_norm, const void* w_gate_up,
+                              void* out, void* stream);
+
 /* Which variant a forward of num_tokens tokens runs on, in *variant (a qkv_variant).
  * Host-only; returns QKV_ERR_INVALID_ARG for a bad plan or num_tokens out of range. */
 qkv_status qkv_plan_variant(qkv_plan plan, int64_t num_tokens, int32_t* variant);

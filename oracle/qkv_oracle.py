@@ -143,3 +143,34 @@ def kv_cache_write(cache, slots, rows):
             seen.add(s)
             out[s] = rows[t]
     return out
+
+
+def silu(z):
+    """SiLU (swish): z / (1 + exp(-z)); exp overflow for very negative z gives -0."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_parts(x, w_norm, w_gate_up, eps: float):
+    """The gate and up sums (g, u), each [T, I] float64, before the SiLU and product."""
+    act = rms_norm(x, w_norm, eps)
+    y = act @ np.asarray(w_gate_up, dtype=np.float64)
+    assert y.shape[1] % 2 == 0, "W_gate_up must have an even number of columns"
+    inter = y.shape[1] // 2
+    gate, up = y[:, :inter], y[:, inter:]
+    return gate, up
+
+
+def swiglu_forward(x, w_norm, w_gate_up, eps: float):
+    """Gated MLP input of the decoder layer: out [T, I] in float64.
+
+    The operator-fusion section ("算子融合") of the page "Liger-Kernel核心技术：
+    RollingBuffer与融合算子详解" (Liger-Kernel core techniques: RollingBuffer and
+    fused operators explained) describes the fused linear SwiGLU: the input times the
+    gate weight and times the up weight, SiLU of the first times the second.  Here its
+    input is the layer's RMSNorm output, computed as in qkv_forward, and the two
+    weights are one [H, 2I] matrix with the gate columns first.  No bias.
+    """
+    gate, up = swiglu_parts(x, w_norm, w_gate_up, eps)
+    return silu(gate) * up

@@ -356,4 +356,56 @@ def pin_kv_cache_untouched_and_dropped(o):
     _close(out, expect, 0.0, "cache rows")
 
 
+def _silu_tanh(z):
+    """SiLU through the identity sigmoid(z) = (1 + tanh(z/2)) / 2."""
+    return z * 0.5 * (1.0 + np.tanh(0.5 * z))
+
+
+def pin_silu_values(o):
+    """SiLU(0) = 0; SiLU(1) = e/(e+1); SiLU(z) - SiLU(-z) = z; the tanh form of the
+    logistic function agrees everywhere."""
+    _close(o.silu(np.array([0.0]))[0], 0.0, 0.0, "silu(0)")
+    e = np.e
+    _close(o.silu(np.array([1.0]))[0], e / (e + 1.0), 1e-15, "silu(1)")
+    z = np.linspace(-30.0, 30.0, 241)
+    _close(o.silu(z) - o.silu(-z), z, 1e-12, "odd part")
+    _close(o.silu(z), _silu_tanh(z), 1e-12, "tanh form")
+
+
+def pin_swiglu_brute_force(o):
+    """Triple loops (row norm, both dot products, tanh-form SiLU) on a tiny case."""
+    rng = _rng(51)
+    T, H, inter, eps = 3, 8, 5, 1e-5
+    x = rng.standard_normal((T, H)) * np.array([[0.1], [1.0], [7.0]])
+    w = 1.0 + 0.1 * rng.standard_normal(H)
+    W = 0.3 * rng.standard_normal((H, 2 * inter))
+    ref = np.zeros((T, inter))
+    for t in range(T):
+        ms = sum(x[t, k] ** 2 for k in range(H)) / H
+        r = 1.0 / np.sqrt(ms + eps)
+        a = [x[t, k] * r * w[k] for k in range(H)]
+        for j in range(inter):
+            g = sum(a[k] * W[k, j] for k in range(H))
+            u = sum(a[k] * W[k, inter + j] for k in range(H))
+            ref[t, j] = _silu_tanh(g) * u
+    _close(o.swiglu_forward(x, w, W, eps), ref, 1e-12, "swiglu brute force")
+
+
+def pin_swiglu_onehot_layout(o):
+    """Gate column j0 reads input feature k0 and up column j0 reads k1: output j0 is
+    SiLU(a[:, k0]) * a[:, k1] and every other output is 0 (gate columns come first)."""
+    rng = _rng(52)
+    T, H, inter, eps = 4, 6, 3, 1e-6
+    x = rng.standard_normal((T, H))
+    w = np.ones(H)
+    W = np.zeros((H, 2 * inter))
+    k0, k1, j0 = 2, 5, 1
+    W[k0, j0] = 1.0
+    W[k1, inter + j0] = 1.0
+    a = x / np.sqrt((x * x).mean(axis=1, keepdims=True) + eps)
+    expect = np.zeros((T, inter))
+    expect[:, j0] = _silu_tanh(a[:, k0]) * a[:, k1]
+    _close(o.swiglu_forward(x, w, W, eps), expect, 1e-12, "swiglu one-hot")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

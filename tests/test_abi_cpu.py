@@ -124,3 +124,25 @@ def test_ring_slots_helper():
     assert got.tolist() == [100, 101, 104, 100, 104, 100, 104]
     with pytest.raises(ValueError):
         qkv.ring_slots(pos, 0)
+
+
+def test_swiglu_arguments_rejected_before_any_hip_call():
+    """The stateless gated-MLP call validates sizes, dtype, eps and pointers first; shapes
+    the kernel does not implement are QKV_ERR_UNSUPPORTED, all without touching a GPU."""
+    lib = qkv.load_library()
+    fake = 1 << 20  # 16-byte aligned, never dereferenced: every case below fails validation
+    ok_ptrs = [fake] * 4
+    bf16 = qkv.QKV_BF16
+    assert lib.qkv_swiglu_forward(0, 4096, 11008, bf16, 1e-6, *([None] * 4), None) == qkv.QKV_OK
+    assert lib.qkv_swiglu_forward(-1, 4096, 11008, bf16, 1e-6, *ok_ptrs, None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_swiglu_forward(4, 0, 11008, bf16, 1e-6, *ok_ptrs, None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_swiglu_forward(4, 4096, 11008, 7, 1e-6, *ok_ptrs, None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_swiglu_forward(4, 4096, 11008, bf16, -1.0, *ok_ptrs, None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_swiglu_forward(4, 4096, 11008, bf16, float("nan"), *ok_ptrs, None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_swiglu_forward(4, 4096, 11008, bf16, 1e-6, None, fake, fake, fake, None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_swiglu_forward(4, 4096, 11008, bf16, 1e-6, fake + 2, fake, fake, fake, None) == \
+        qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_swiglu_forward(4, 4096, 11008, qkv.QKV_F32, 1e-6, *ok_ptrs, None) == qkv.QKV_ERR_UNSUPPORTED
+    assert lib.qkv_swiglu_forward(4, 4000, 11008, bf16, 1e-6, *ok_ptrs, None) == qkv.QKV_ERR_UNSUPPORTED
+    assert lib.qkv_swiglu_forward(4, 4096, 11000, bf16, 1e-6, *ok_ptrs, None) == qkv.QKV_ERR_UNSUPPORTED
+    assert lib.qkv_swiglu_forward(1 << 20, 4096, 11008, bf16, 1e-6, *ok_ptrs, None) == qkv.QKV_ERR_UNSUPPORTED

@@ -40,6 +40,12 @@ MUTANTS = {
     "cache_cleared": [("out = np.array(cache, dtype=np.float64, copy=True)",
                        "out = np.zeros_like(np.asarray(cache, dtype=np.float64))")],
     "cache_token_order_reversed": [("out[s] = rows[t]", "out[s] = rows[slots.shape[0] - 1 - t]")],
+    "swiglu_gate_up_swapped": [("gate, up = y[:, :inter], y[:, inter:]", "up, gate = y[:, :inter], y[:, inter:]")],
+    "swiglu_sigmoid_only": [("return silu(gate) * up", "return up / (1.0 + np.exp(-gate))")],
+    "swiglu_silu_sign": [("return z / (1.0 + np.exp(-z))", "return z / (1.0 + np.exp(z))")],
+    "swiglu_no_norm": [("act = rms_norm(x, w_norm, eps)",
+                        "act = np.asarray(x, dtype=np.float64) * np.asarray(w_norm, dtype=np.float64)")],
+    "swiglu_interleaved_halves": [("gate, up = y[:, :inter], y[:, inter:]", "gate, up = y[:, 0::2], y[:, 1::2]")],
     "k_v_swapped": [("k = rope(y[:, n_q:n_q + n_kv], pos, head_dim, theta)",
                      "k = rope(y[:, n_q + n_kv:], pos, head_dim, theta)"),
                     ("v = y[:, n_q + n_kv:].copy()", "v = y[:, n_q:n_q + n_kv].copy()")],

@@ -27,6 +27,8 @@ EXPORTS = {
     "qkv_forward": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qkv_forward_kv_cache": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
                                             _vp, _vp, _vp, _vp]),
+    "qkv_swiglu_forward": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_double, _vp, _vp, _vp, _vp, _vp]),
     "qkv_rms_inv": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp]),
     "qkv_plan_variant": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)]),
     "qkv_plan_destroy": (ctypes.c_int, [_vp]),
@@ -100,6 +102,27 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 def _stream_handle(stream: Optional[torch.cuda.Stream]) -> int:
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+def swiglu_forward(x: torch.Tensor, w_norm: torch.Tensor, w_gate_up: torch.Tensor, eps: float,
+                   out: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """RMSNorm then SiLU(a @ W_gate) * (a @ W_up) in one launch; w_gate_up is [H, 2I]
+    with the gate columns first.  Returns out [T, I] (bf16)."""
+    lib = load_library()
+    for name, t in (("x", x), ("w_norm", w_norm), ("w_gate_up", w_gate_up)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    T, H = x.shape
+    if w_norm.shape != (H,) or w_gate_up.dim() != 2 or w_gate_up.shape[0] != H or w_gate_up.shape[1] % 2:
+        raise ValueError("shapes must be x [T, H], w_norm [H], w_gate_up [H, 2I]")
+    I = w_gate_up.shape[1] // 2
+    if out is None:
+        out = torch.empty((T, I), dtype=x.dtype, device=x.device)
+    if out.shape != (T, I) or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [T, I] tensor of x's dtype")
+    _check(lib.qkv_swiglu_forward(T, H, I, _dtype_code(x.dtype), float(eps), _ptr(x), _ptr(w_norm),
+                                  _ptr(w_gate_up), _ptr(out), _stream_handle(stream)), "qkv_swiglu_forward")
+    return out
 
 
 def ring_slots(pos: torch.Tensor, capacity: int, first_row: int = 0) -> torch.Tensor:

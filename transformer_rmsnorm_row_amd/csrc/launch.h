@@ -36,6 +36,10 @@ hipError_t launch_generic(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
 bool prefill_supports(int H, int N, int Nq, int Nkv, int d);
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
+// gated MLP on the prefill kernel: x, w_norm, w = [H, 2I] (gate | up), q = out [T, I],
+// N = 2I, T, H, eps, bf16
+hipError_t launch_swiglu(const ForwardArgs& a, hipStream_t stream);
+bool swiglu_supports(int H, int I);
 bool decode_supports(int T, int H, int N, int Nq, int Nkv, int d);
 // fp32 elements of plan scratch the decode kernel needs (partials + sums of squares)
 size_t decode_scratch_floats(int H, int N);

@@ -108,6 +108,11 @@ __device__ __forceinline__ float turn_fraction(int32_t pos, double rev) {
 template <int P>
 using Int = std::integral_constant<int, P>;
 
+// Epilogues sharing the normalise-on-load GEMM: the attention-input chain (bias,
+// rotary embedding, Q/K/V stores) and the gated MLP (SiLU(gate) * up).
+constexpr int kEpiQkv = 0, kEpiSwiglu = 1;
+
+template <int kEpi>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
 
@@ -149,7 +154,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const uint32_t krow = 2u * i + (lane >> 5);  // row within the 4-row swizzle period
-    b_voff[i] = ((4u * wave + krow) * N + n0 + 8u * wchunk(krow, lane & 31)) * 2u;
+    uint32_t col = n0 + 8u * wchunk(krow, lane & 31);
+    if constexpr (kEpi == kEpiSwiglu) {
+      // tile tn covers features 128 tn .. +127; its "head" h (128 columns) holds gate
+      // features 64h .. +63 in columns 0-63 and the same up features in 64-127, so each
+      // lane's column pair (j, j + 64) is (gate, up) of one feature
+      const uint32_t lc = wchunk(krow, lane & 31), h = lc >> 4, wi = (lc & 15u) * 8u;
+      const uint32_t f = 128u * (uint32_t)tn + 64u * h + (wi & 63u);
+      col = wi < 64u ? f : (uint32_t)(N / 2) + f;
+    }
+    b_voff[i] = ((4u * wave + krow) * N + col) * 2u;
   }
   const uint64_t wbase = reinterpret_cast<uint64_t>(a.w);
   const u32x4 w_rsrc = {(uint32_t)wbase, (uint32_t)(wbase >> 32), (uint32_t)H * (uint32_t)N * 2u,
@@ -325,17 +339,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   // without bias reads 0 through an empty range), so nothing waits for them before
   // their first use in the epilogue.
   const int hcol = n0 + head * 128;  // first column of this wave's head
-  const int32_t pos_pref =
-      __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.pos, (uint32_t)T * 4u), (int)((uint32_t)(m0 + (tid & (BM - 1))) * 4u), 0, 0);
-  const int32_t slot_pref = __builtin_amdgcn_raw_buffer_load_b32(
-      make_rsrc(a.slots ? a.slots : a.pos, a.slots ? (uint32_t)T * 4u : 0u), (int)((uint32_t)(m0 + (tid & (BM - 1))) * 4u), 0, 0);
-  const auto b_rsrc = make_rsrc(a.bias ? a.bias : a.w, a.bias ? (uint32_t)N * 2u : 0u);
-  uint16_t braw[2];
+  int32_t pos_pref = 0, slot_pref = -1;
+  uint16_t braw[2] = {0, 0};
+  uint64_t rev_bits = 0;
+  if constexpr (kEpi == kEpiQkv) {
+    pos_pref = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.pos, (uint32_t)T * 4u),
+                                                    (int)((uint32_t)(m0 + (tid & (BM - 1))) * 4u), 0, 0);
+    slot_pref = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.slots ? a.slots : a.pos, a.slots ? (uint32_t)T * 4u : 0u),
+                                                     (int)((uint32_t)(m0 + (tid & (BM - 1))) * 4u), 0, 0);
+    const auto b_rsrc = make_rsrc(a.bias ? a.bias : a.w, a.bias ? (uint32_t)N * 2u : 0u);
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-    braw[cb] = __builtin_amdgcn_raw_buffer_load_b16(b_rsrc, (int)((uint32_t)(hcol + c0 + cb * 64 + fl) * 2u), 0, 0);
-  const uint64_t rev_bits = __builtin_bit_cast(
-      uint64_t, __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(a.rev_freq, 64u * 8u), (int)((uint32_t)(c0 + fl) * 8u), 0, 0));
+    for (int cb = 0; cb < 2; ++cb)
+      braw[cb] = __builtin_amdgcn_raw_buffer_load_b16(b_rsrc, (int)((uint32_t)(hcol + c0 + cb * 64 + fl) * 2u), 0, 0);
+    rev_bits = __builtin_bit_cast(
+        uint64_t, __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(a.rev_freq, 64u * 8u), (int)((uint32_t)(c0 + fl) * 8u), 0, 0));
+  }
   // prologue: W(0..2) and x(0..1) issued, x(0) converted into activation slot 0
   issue_w(0, 0);
   issue_x(0, 0);
@@ -405,72 +423,107 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   }
   __syncthreads();
 
-  // ---- epilogue: scale, bias, rotate, stage as bf16, store
-  const float bcol[2] = {bf16_to_f32(braw[0]), bf16_to_f32(braw[1])};
-  const double rev = __builtin_bit_cast(double, rev_bits);
-  const bool rotate = hcol < a.Nq + a.Nkv;
-  void* out;
-  uint32_t width, ocol;
-  if (hcol < a.Nq) {
-    out = a.q; width = a.Nq; ocol = hcol;
-  } else if (hcol < a.Nq + a.Nkv) {
-    out = a.k; width = a.Nkv; ocol = hcol - a.Nq;
-  } else {
-    out = a.v; width = a.Nkv; ocol = hcol - a.Nq - a.Nkv;
-  }
-
-  uint8_t* stage = smem + (grp * 2 + head) * kBlockStage;
-  // one instantiation per case, so the uniform test is not repeated (as a branch)
-  // around every element and independent elements can overlap
-  auto scale_rotate_stage = [&](auto RotC) {
-    constexpr bool kRot = decltype(RotC)::value;
+  if constexpr (kEpi == kEpiSwiglu) {
+    // ---- epilogue: out = SiLU(g) * u with g, u the gate and up sums scaled by 1/rms;
+    // staged as bf16 per (row half, head) block of 64 features, stored with 16-byte writes
+    uint8_t* stage = smem + (grp * 2 + head) * kBlockStage;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int rbase = rb * 32 + rg * 8 + (int)fh * 4;  // row within the group's 128
         const f32x4 ri4 = *reinterpret_cast<const f32x4*>(s_rinv + grp * 128 + rbase);
-        const i32x4 p4 = *reinterpret_cast<const i32x4*>(s_pos + grp * 128 + rbase);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          float y0 = fmaf(acc[rb][0][rg * 4 + rr], ri4[rr], bcol[0]);
-          float y1 = fmaf(acc[rb][1][rg * 4 + rr], ri4[rr], bcol[1]);
-          if constexpr (kRot) {
-            const float tf = turn_fraction(p4[rr], rev);
-            const float c = __builtin_amdgcn_cosf(tf), s = __builtin_amdgcn_sinf(tf);
-            const float u0 = y0, v0 = y1;
-            y0 = u0 * c - v0 * s;
-            y1 = v0 * c + u0 * s;
-          }
-          uint16_t* srow = reinterpret_cast<uint16_t*>(stage + (rbase + rr) * kStagePitch);
-          srow[c0 + fl] = f32_to_bf16(y0);
-          srow[c0 + 64 + fl] = f32_to_bf16(y1);
+          const float g = acc[rb][0][rg * 4 + rr] * ri4[rr];
+          const float u = acc[rb][1][rg * 4 + rr] * ri4[rr];
+          const float o = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+          reinterpret_cast<uint16_t*>(stage + (rbase + rr) * kStagePitch)[c0 + fl] = f32_to_bf16(o);
         }
       }
     }
-  };
-  if (rotate)
-    scale_rotate_stage(std::true_type{});
-  else
-    scale_rotate_stage(std::false_type{});
-  __syncthreads();
-  // wave (grp, slot) stores rows 64 (slot % 2) .. +63 of its (group, head) block.
-  // K and V rows go to their cache slots when the forward has them; a row index of
-  // out_rows or more lies past the buffer's range, so that store is dropped.
-  const bool to_cache = a.slots != nullptr && hcol >= a.Nq;
-  const uint32_t out_rows = to_cache ? (uint32_t)a.cache_rows : (uint32_t)T;
-  const auto ro = make_rsrc(out, out_rows * width * 2u);
-  const uint32_t ch = lane & 15;
+    __syncthreads();
+    // wave (grp, slot) stores rows 64 (slot % 2) .. +63 of its (group, head) block:
+    // 8 lanes of 16 bytes per 128-byte row
+    const uint32_t I = (uint32_t)N / 2u;
+    const uint32_t fcol = 128u * (uint32_t)tn + 64u * (uint32_t)head;
+    const auto ro = make_rsrc(a.q, (uint32_t)T * I * 2u);
+    const uint32_t ch = lane & 7;
 #pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const uint32_t row = 64u * (slot & 1) + 4u * it + (lane >> 4);
-    const u32x4 v = lds_read16(stage, row * kStagePitch + ch * 16u);
-    uint32_t orow = (uint32_t)(m0 + 128 * grp) + row;
-    if (to_cache) {
-      const int32_t sr = s_slot[128 * grp + row];
-      orow = sr >= 0 && sr < a.cache_rows ? (uint32_t)sr : out_rows;
+    for (int it = 0; it < 8; ++it) {
+      const uint32_t row = 64u * (slot & 1) + 8u * it + (lane >> 3);
+      const u32x4 v = lds_read16(stage, row * kStagePitch + ch * 16u);
+      const uint32_t grow = (uint32_t)(m0 + 128 * grp) + row;
+      buf_store16(v, ro, (grow * I + fcol + ch * 8u) * 2u);
     }
-    buf_store16(v, ro, (orow * width + ocol + ch * 8u) * 2u);
+  } else {
+    // ---- epilogue: scale, bias, rotate, stage as bf16, store
+    const float bcol[2] = {bf16_to_f32(braw[0]), bf16_to_f32(braw[1])};
+    const double rev = __builtin_bit_cast(double, rev_bits);
+    const bool rotate = hcol < a.Nq + a.Nkv;
+    void* out;
+    uint32_t width, ocol;
+    if (hcol < a.Nq) {
+      out = a.q; width = a.Nq; ocol = hcol;
+    } else if (hcol < a.Nq + a.Nkv) {
+      out = a.k; width = a.Nkv; ocol = hcol - a.Nq;
+    } else {
+      out = a.v; width = a.Nkv; ocol = hcol - a.Nq - a.Nkv;
+    }
+
+    uint8_t* stage = smem + (grp * 2 + head) * kBlockStage;
+    // one instantiation per case, so the uniform test is not repeated (as a branch)
+    // around every element and independent elements can overlap
+    auto scale_rotate_stage = [&](auto RotC) {
+      constexpr bool kRot = decltype(RotC)::value;
+  #pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+  #pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int rbase = rb * 32 + rg * 8 + (int)fh * 4;  // row within the group's 128
+          const f32x4 ri4 = *reinterpret_cast<const f32x4*>(s_rinv + grp * 128 + rbase);
+          const i32x4 p4 = *reinterpret_cast<const i32x4*>(s_pos + grp * 128 + rbase);
+  #pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            float y0 = fmaf(acc[rb][0][rg * 4 + rr], ri4[rr], bcol[0]);
+            float y1 = fmaf(acc[rb][1][rg * 4 + rr], ri4[rr], bcol[1]);
+            if constexpr (kRot) {
+              const float tf = turn_fraction(p4[rr], rev);
+              const float c = __builtin_amdgcn_cosf(tf), s = __builtin_amdgcn_sinf(tf);
+              const float u0 = y0, v0 = y1;
+              y0 = u0 * c - v0 * s;
+              y1 = v0 * c + u0 * s;
+            }
+            uint16_t* srow = reinterpret_cast<uint16_t*>(stage + (rbase + rr) * kStagePitch);
+            srow[c0 + fl] = f32_to_bf16(y0);
+            srow[c0 + 64 + fl] = f32_to_bf16(y1);
+          }
+        }
+      }
+    };
+    if (rotate)
+      scale_rotate_stage(std::true_type{});
+    else
+      scale_rotate_stage(std::false_type{});
+    __syncthreads();
+    // wave (grp, slot) stores rows 64 (slot % 2) .. +63 of its (group, head) block.
+    // K and V rows go to their cache slots when the forward has them; a row index of
+    // out_rows or more lies past the buffer's range, so that store is dropped.
+    const bool to_cache = a.slots != nullptr && hcol >= a.Nq;
+    const uint32_t out_rows = to_cache ? (uint32_t)a.cache_rows : (uint32_t)T;
+    const auto ro = make_rsrc(out, out_rows * width * 2u);
+    const uint32_t ch = lane & 15;
+  #pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const uint32_t row = 64u * (slot & 1) + 4u * it + (lane >> 4);
+      const u32x4 v = lds_read16(stage, row * kStagePitch + ch * 16u);
+      uint32_t orow = (uint32_t)(m0 + 128 * grp) + row;
+      if (to_cache) {
+        const int32_t sr = s_slot[128 * grp + row];
+        orow = sr >= 0 && sr < a.cache_rows ? (uint32_t)sr : out_rows;
+      }
+      buf_store16(v, ro, (orow * width + ocol + ch * 8u) * 2u);
+    }
   }
 }
 
@@ -482,7 +535,16 @@ bool prefill_supports(int H, int N, int Nq, int Nkv, int d) {
 
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream) {
   const int tiles_m = (a.T + BM - 1) / BM, tiles_n = a.N / BN;
-  prefill_kernel<<<dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
+  prefill_kernel<kEpiQkv><<<dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+bool swiglu_supports(int H, int I) { return H % (4 * BK) == 0 && I % 128 == 0; }
+
+hipError_t launch_swiglu(const ForwardArgs& a, hipStream_t stream) {
+  // a.N = 2I columns of [gate | up]; the output (a.q) is [T, I]
+  const int tiles_m = (a.T + BM - 1) / BM, tiles_n = a.N / BN;
+  prefill_kernel<kEpiSwiglu><<<dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -273,6 +273,35 @@ qkv_status qkv_plan_destroy(qkv_plan plan) {
   return QKV_OK;
 }
 
+qkv_status qkv_swiglu_forward(int64_t num_tokens, int32_t hidden, int32_t intermediate, int32_t dtype, double eps,
+                              const void* x, const void* w_norm, const void* w_gate_up, void* out, void* stream) {
+  if (num_tokens < 0 || hidden < 1 || intermediate < 1) return QKV_ERR_INVALID_ARG;
+  if (dtype != QKV_F32 && dtype != QKV_BF16) return QKV_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.0) return QKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return QKV_OK;
+  if (!x || !w_norm || !w_gate_up || !out) return QKV_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w_norm, 16) || !aligned(w_gate_up, 16) || !aligned(out, 16))
+    return QKV_ERR_INVALID_ARG;
+  if (dtype != QKV_BF16 || !qkv::swiglu_supports(hidden, intermediate)) return QKV_ERR_UNSUPPORTED;
+  const int64_t H = hidden, I = intermediate;
+  if (num_tokens * H * 2 >= kMaxBytes || H * 2 * I * 2 >= kMaxBytes || num_tokens * I * 2 >= kMaxBytes)
+    return QKV_ERR_UNSUPPORTED;
+  qkv::ForwardArgs a{};
+  a.x = x;
+  a.w_norm = w_norm;
+  a.w = w_gate_up;
+  a.q = out;
+  a.T = (int)num_tokens;
+  a.H = hidden;
+  a.N = 2 * intermediate;
+  a.Nq = intermediate;
+  a.d = 128;
+  a.eps = (float)eps;
+  a.bf16 = true;
+  const hipError_t e = qkv::launch_swiglu(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
+}
+
 const char* qkv_status_string(qkv_status status) {
   switch (status) {
     case QKV_OK: return "ok";

@@ -125,3 +125,44 @@ def digest(t: Optional[torch.Tensor]) -> str:
     if t is None:
         return "-"
     return hashlib.sha256(t.contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()[:16]
+
+
+@dataclasses.dataclass(frozen=True)
+class MlpWorkload:
+    """Gated-MLP input of one Llama-style layer: RMSNorm, then [H, 2I] gate|up weights."""
+    name: str
+    batch: int
+    seq: int
+    hidden: int
+    intermediate: int
+    eps: float
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seq
+
+    def flops(self, T: Optional[int] = None) -> int:
+        """Dense contraction flops of one forward (2*T*H*2I)."""
+        T = self.tokens if T is None else T
+        return 2 * T * self.hidden * 2 * self.intermediate
+
+    def algorithmic_bytes(self, T: Optional[int] = None) -> int:
+        """One read of x, w_norm and the gate|up weights, one write of the output (bf16)."""
+        T = self.tokens if T is None else T
+        H, inter = self.hidden, self.intermediate
+        return 2 * (T * H + H + H * 2 * inter + T * inter)
+
+
+# Llama-7B MLP shape at the page's "seq_len 2k, hidden 4096" SwiGLU comparison, batch 4
+MLP_WORKLOADS = {
+    "llama7b_mlp": MlpWorkload("llama7b_mlp", 4, 2048, 4096, 11008, 1e-6),
+}
+
+
+def make_mlp_inputs(wl: MlpWorkload, seed: int = 6000) -> dict:
+    """Host bf16 tensors: x ~ N(0,1), w_norm ~ 1 + N(0, 0.1), W_gate_up ~ N(0, 0.02)."""
+    T, H, inter = wl.tokens, wl.hidden, wl.intermediate
+    x = torch.randn(T, H, generator=_gen(seed + 1), dtype=torch.float32).to(torch.bfloat16)
+    w_gate_up = (torch.randn(H, 2 * inter, generator=_gen(seed + 2), dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    w_norm = (1.0 + 0.1 * torch.randn(H, generator=_gen(seed + 3), dtype=torch.float32)).to(torch.bfloat16)
+    return {"x": x, "w_norm": w_norm, "w_gate_up": w_gate_up}
