@@ -312,6 +312,8 @@ def main() -> int:
     ap.add_argument("--workload", default="llama7b_prefill")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the key/value-cache and gated-MLP legs (time only the workload's own forward)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (steps times), to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings against a known byte count")
@@ -347,7 +349,7 @@ def main() -> int:
     cold = None
     if wl.tokens > 256:
         cold = time_forward_cold(plan, bufs)
-    cache_s = time_forward_kv_cache(qkv, wl, plan, bufs, args.steps, args.warmup)
+    cache_s = None if args.no_extra else time_forward_kv_cache(qkv, wl, plan, bufs, args.steps, args.warmup)
     plan.close()
 
     flops = wl.flops()
@@ -381,10 +383,11 @@ def main() -> int:
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_us": round(kernel_s * 1e6, 2), "algorithmic_bytes": nbytes, "flops": flops},
     }
-    out["kv_cache"] = {"us": round(cache_s * 1e6, 2), "tflops": round(flops / cache_s / 1e12, 2),
-                       "time_vs_dense": round(cache_s / kernel_s, 4),
-                       "cache": "K and V rows written to slot = sequence's first row + position mod C "
-                                "of [batch x C, kv_heads*head_dim] caches, C = max(4096, seq_len)"}
+    if cache_s is not None:
+        out["kv_cache"] = {"us": round(cache_s * 1e6, 2), "tflops": round(flops / cache_s / 1e12, 2),
+                           "time_vs_dense": round(cache_s / kernel_s, 4),
+                           "cache": "K and V rows written to slot = sequence's first row + position mod C "
+                                    "of [batch x C, kv_heads*head_dim] caches, C = max(4096, seq_len)"}
     if cold:
         pct = lambda p: cold[min(len(cold) - 1, int(round(p * (len(cold) - 1))))]
         med = pct(0.5)
@@ -396,7 +399,7 @@ def main() -> int:
     if not args.no_decode and wl.name != "gqa_decode":
         print("[bench] decode leg", file=sys.stderr, flush=True)
         out["decode"] = decode_leg(qkv, workloads)
-    if not args.no_decode and wl.name != "gqa_decode":
+    if not args.no_extra and wl.name != "gqa_decode":
         print("[bench] gated-MLP leg", file=sys.stderr, flush=True)
         out["swiglu"] = swiglu_leg(qkv, workloads)
     if not args.no_cpu_baseline:
