@@ -174,3 +174,48 @@ def swiglu_forward(x, w_norm, w_gate_up, eps: float):
     """
     gate, up = swiglu_parts(x, w_norm, w_gate_up, eps)
     return silu(gate) * up
+
+
+def qkv_backward(x, w_norm, w_qkv, pos, gq, gk, gv, num_q_heads: int, num_kv_heads: int,
+                 head_dim: int, eps: float, theta: float, with_bias: bool = False):
+    """Gradients of the chain for upstream gradients gq, gk, gv of Q, K, V.
+
+    The operator-fusion section ("算子融合") of the page "Liger-Kernel核心技术：
+    RollingBuffer与融合算子详解" reports backward speed-ups for its fused kernels
+    alongside the forward ones; the backward of this chain is the chain rule applied
+    to the forward above, written out step by step in float64:
+
+      * rotation: the transpose of a rotation by +angle is the rotation by -angle,
+        so gy = (gu cos + gv sin, gv cos - gu sin) on each Q/K pair; gy = gv on V;
+      * bias: db[n] = sum_t gy[t, n];
+      * projection: dW = a^T gy, ga = gy W^T;
+      * RMSNorm a = x r w with r = (mean x^2 + eps)^(-1/2), dr/dx_j = -r^3 x_j / H:
+        dw[k] = sum_t ga[t,k] x[t,k] r[t];
+        dx[t,j] = r w_j ga_j - (r^3 / H) x_j sum_k ga_k w_k x_k.
+
+    Returns (dx, dw_norm, dw_qkv, dbias or None), float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_norm, dtype=np.float64)
+    W = np.asarray(w_qkv, dtype=np.float64)
+    T, H = x.shape
+    half = head_dim // 2
+    phi = rope_angles(pos, head_dim, theta)[:, None, :]
+    c, s = np.cos(phi), np.sin(phi)
+
+    def unrotate(g):
+        heads = np.asarray(g, dtype=np.float64).reshape(T, -1, head_dim)
+        gu, gv_ = heads[..., :half], heads[..., half:]
+        return np.concatenate([gu * c + gv_ * s, gv_ * c - gu * s], axis=-1).reshape(T, -1)
+
+    gy = np.concatenate([unrotate(gq), unrotate(gk), np.asarray(gv, dtype=np.float64)], axis=1)
+    assert gy.shape[1] == W.shape[1], "upstream gradients must cover every column of W_qkv"
+    db = gy.sum(axis=0) if with_bias else None
+    r = inv_rms(x, eps)
+    a = x * r[:, None] * w[None, :]
+    dW = a.T @ gy
+    ga = gy @ W.T
+    dw = np.sum(ga * x * r[:, None], axis=0)
+    inner = np.sum(ga * w[None, :] * x, axis=1)
+    dx = r[:, None] * w[None, :] * ga - (r ** 3 / H)[:, None] * x * inner[:, None]
+    return dx, dw, dW, db

@@ -408,4 +408,57 @@ def pin_swiglu_onehot_layout(o):
     _close(o.swiglu_forward(x, w, W, eps), expect, 1e-12, "swiglu one-hot")
 
 
+def pin_backward_finite_differences(o):
+    """Every gradient of the backward against central differences of the forward on a
+    tiny case (loss = sum of upstream gradient times output), with a bias."""
+    rng = _rng(61)
+    T, H, nq, nkv, d, eps, theta = 3, 8, 2, 1, 4, 1e-3, 100.0
+    N = (nq + 2 * nkv) * d
+    x = rng.standard_normal((T, H))
+    w = 1.0 + 0.2 * rng.standard_normal(H)
+    W = 0.5 * rng.standard_normal((H, N))
+    b = 0.3 * rng.standard_normal(N)
+    pos = np.array([0, 5, 11])
+    gq = rng.standard_normal((T, nq * d))
+    gk = rng.standard_normal((T, nkv * d))
+    gv = rng.standard_normal((T, nkv * d))
+
+    def loss(x_, w_, W_, b_):
+        q, k, v = o.qkv_forward(x_, w_, W_, b_, pos, nq, nkv, d, eps, theta)
+        return float(np.sum(q * gq) + np.sum(k * gk) + np.sum(v * gv))
+
+    def fd(arr, f):
+        g = np.zeros_like(arr)
+        h = 1e-6
+        for idx in np.ndindex(arr.shape):
+            p, m = arr.copy(), arr.copy()
+            p[idx] += h
+            m[idx] -= h
+            g[idx] = (f(p) - f(m)) / (2 * h)
+        return g
+
+    dx, dw, dW, db = o.qkv_backward(x, w, W, pos, gq, gk, gv, nq, nkv, d, eps, theta, with_bias=True)
+    _close(dx, fd(x, lambda v_: loss(v_, w, W, b)), 1e-6, "dx")
+    _close(dw, fd(w, lambda v_: loss(x, v_, W, b)), 1e-6, "dw_norm")
+    _close(dW, fd(W, lambda v_: loss(x, w, v_, b)), 1e-6, "dW")
+    _close(db, fd(b, lambda v_: loss(x, w, W, v_)), 1e-6, "db")
+
+
+def pin_backward_scale_invariance(o):
+    """With eps = 0 the norm's output does not change when a row is scaled, so the input
+    gradient of every token is orthogonal to that token's row: sum_j x_j dx_j = 0."""
+    rng = _rng(62)
+    T, H, nq, nkv, d = 4, 16, 2, 2, 8
+    N = (nq + 2 * nkv) * d
+    x = rng.standard_normal((T, H)) * np.array([[0.01], [1.0], [3.0], [100.0]])
+    w = 1.0 + 0.1 * rng.standard_normal(H)
+    W = 0.2 * rng.standard_normal((H, N))
+    pos = np.array([3, 0, 7, 1000])
+    g = [rng.standard_normal((T, n)) for n in (nq * d, nkv * d, nkv * d)]
+    dx, _, _, db = o.qkv_backward(x, w, W, pos, *g, nq, nkv, d, 0.0, 1e4)
+    assert db is None
+    dots = np.sum(dx * x, axis=1) / (np.linalg.norm(dx, axis=1) * np.linalg.norm(x, axis=1))
+    _close(dots, np.zeros(T), 1e-12, "x . dx")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

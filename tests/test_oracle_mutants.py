@@ -46,6 +46,12 @@ MUTANTS = {
     "swiglu_no_norm": [("act = rms_norm(x, w_norm, eps)",
                         "act = np.asarray(x, dtype=np.float64) * np.asarray(w_norm, dtype=np.float64)")],
     "swiglu_interleaved_halves": [("gate, up = y[:, :inter], y[:, inter:]", "gate, up = y[:, 0::2], y[:, 1::2]")],
+    "bwd_rotation_not_inverted": [("[gu * c + gv_ * s, gv_ * c - gu * s]", "[gu * c - gv_ * s, gv_ * c + gu * s]")],
+    "bwd_norm_term_dropped": [("- (r ** 3 / H)[:, None] * x * inner[:, None]", "")],
+    "bwd_norm_weight_missing_in_inner": [("inner = np.sum(ga * w[None, :] * x, axis=1)", "inner = np.sum(ga * x, axis=1)")],
+    "bwd_dw_without_r": [("dw = np.sum(ga * x * r[:, None], axis=0)", "dw = np.sum(ga * x, axis=0)")],
+    "bwd_dW_from_rotated_grads": [("dW = a.T @ gy", "dW = a.T @ np.concatenate([np.asarray(gq), np.asarray(gk), "
+                                                    "np.asarray(gv)], axis=1)")],
     "k_v_swapped": [("k = rope(y[:, n_q:n_q + n_kv], pos, head_dim, theta)",
                      "k = rope(y[:, n_q + n_kv:], pos, head_dim, theta)"),
                     ("v = y[:, n_q + n_kv:].copy()", "v = y[:, n_q:n_q + n_kv].copy()")],
