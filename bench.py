@@ -250,6 +250,33 @@ def decode_leg(qkv, workloads, replays: int = 125, copies: int = 8):
     }
 
 
+def backward_leg(qkv, workloads, wl, bufs, steps: int = 10, warmup: int = 2):
+    """The backward of the chain on the workload's shape: unrotate, recomputed
+    activations, two GEMMs (rocBLAS), norm gradient and column sums."""
+    import torch
+    x, w, W, b, pos, q, k, v = bufs
+    g = workloads.make_grads(wl)
+    dq, dk, dv = (g[n].to(x.device) for n in ("dq", "dk", "dv"))
+    plan = qkv.Plan.for_workload(wl)
+    for _ in range(warmup):
+        plan.backward(x, w, W, pos, dq, dk, dv)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        plan.backward(x, w, W, pos, dq, dk, dv)
+    end.record()
+    torch.cuda.synchronize()
+    plan.close()
+    sec = start.elapsed_time(end) / 1e3 / steps
+    gemm_flops = 2 * wl.flops()
+    return {"workload": wl.name, "us": round(sec * 1e6, 2), "gemm_flops": gemm_flops,
+            "tflops": round(gemm_flops / sec / 1e12, 2), "mfma_frac": round(gemm_flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "note": "dW = a^T gy and ga = gy W^T on rocBLAS; unrotate, activations, norm gradient and column "
+                    "sums in this library's kernels"}
+
+
 def swiglu_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
     """The gated-MLP forward (RMSNorm, gate|up GEMM, SiLU(g) * u) on the Llama-7B MLP
     shape, timed with HIP events on the current stream."""
@@ -402,6 +429,8 @@ def main() -> int:
     if not args.no_extra and wl.name != "gqa_decode":
         print("[bench] gated-MLP leg", file=sys.stderr, flush=True)
         out["swiglu"] = swiglu_leg(qkv, workloads)
+        print("[bench] backward leg", file=sys.stderr, flush=True)
+        out["backward"] = backward_leg(qkv, workloads, wl, bufs)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline leg", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_leg(wl, inp)

@@ -143,6 +143,38 @@ qkv_status qkv_forward_kv_cache(qkv_plan plan, int64_t num_tokens,
 qkv_status qkv_rms_inv(qkv_plan plan, int64_t num_tokens, const void* x,
                        float* inv_rms, void* stream);
 
+/* Backward of the chain: given the gradients dq [T, nq*head_dim], dk and dv
+ * [T, nkv*head_dim] of a loss with respect to Q, K and V, write its gradients with
+ * respect to the inputs:
+ *     dx       [T, H]   (overwritten)
+ *     dw_norm  [H]      (overwritten, summed over the T tokens)
+ *     dw_qkv   [H, N]   (overwritten, summed over the T tokens)
+ *     dbias    [N]      (overwritten, summed over the T tokens) -- exactly when the
+ *                       plan has has_bias = 1, NULL otherwise
+ * all in the plan dtype, for the same x, w_norm, w_qkv and pos as the forward (the
+ * bias value does not enter the gradients).  The chain rule, step by step: each
+ * (dq, dk) pair is turned back by -angle (the transpose of the rotation), the bias
+ * gradient is the column sum of that, dW = a^T gy and ga = gy W^T with a = x r w the
+ * normalised activations (recomputed), dw_norm = sum_t ga x r, and
+ * dx_j = r w_j ga_j - (r^3/H) x_j sum_k ga_k w_k x_k.  The page
+ * "Liger-Kernel核心技术：RollingBuffer与融合算子详解" reports backward speed-ups for its
+ * fused kernels next to the forward ones (section "算子融合").
+ * The two products run as rocBLAS GEMMs (bf16 or fp32 operands, fp32 accumulation);
+ * the rest are this library's kernels.  Column sums are done in a fixed order, so
+ * results are deterministic.
+ * Scratch: the first backward call through a plan allocates the plan's backward
+ * scratch (about max_tokens * (N*e + H*e + 4H) bytes, e = element size) and a rocBLAS
+ * handle, kept until qkv_plan_destroy; later calls allocate nothing of their own
+ * (rocBLAS may keep a workspace of its own).  Forwards and backwards through one plan
+ * share scratch and must not overlap in time.
+ * Alignment: every tensor 16-byte aligned except pos (4 bytes).  num_tokens == 0 is a
+ * no-op.  Argument errors return QKV_ERR_INVALID_ARG before any HIP call; failed
+ * scratch allocation QKV_ERR_OUT_OF_MEMORY; launch or rocBLAS failures QKV_ERR_HIP. */
+qkv_status qkv_backward(qkv_plan plan, int64_t num_tokens,
+                        const void* x, const void* w_norm, const void* w_qkv, const int32_t* pos,
+                        const void* dq, const void* dk, const void* dv,
+                        void* dx, void* dw_norm, void* dw_qkv, void* dbias, void* stream);
+
 /* Gated MLP of the same decoder layer on the same normalise-on-load kernel:
  *
  *     r[t]     = 1 / sqrt( (1/H) * sum_k x[t,k]^2 + eps )

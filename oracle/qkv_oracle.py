@@ -177,7 +177,8 @@ def swiglu_forward(x, w_norm, w_gate_up, eps: float):
 
 
 def qkv_backward(x, w_norm, w_qkv, pos, gq, gk, gv, num_q_heads: int, num_kv_heads: int,
-                 head_dim: int, eps: float, theta: float, with_bias: bool = False):
+                 head_dim: int, eps: float, theta: float, with_bias: bool = False,
+                 return_scales: bool = False):
     """Gradients of the chain for upstream gradients gq, gk, gv of Q, K, V.
 
     The operator-fusion section ("算子融合") of the page "Liger-Kernel核心技术：
@@ -193,7 +194,10 @@ def qkv_backward(x, w_norm, w_qkv, pos, gq, gk, gv, num_q_heads: int, num_kv_hea
         dw[k] = sum_t ga[t,k] x[t,k] r[t];
         dx[t,j] = r w_j ga_j - (r^3 / H) x_j sum_k ga_k w_k x_k.
 
-    Returns (dx, dw_norm, dw_qkv, dbias or None), float64.
+    Returns (dx, dw_norm, dw_qkv, dbias or None), float64.  With return_scales, also
+    the root-sum-square of the terms that each element of those gradients sums (over
+    tokens for dw_norm, dW and db; over output columns for dx), the scale that a sum
+    of individually rounded terms is accurate to.
     """
     x = np.asarray(x, dtype=np.float64)
     w = np.asarray(w_norm, dtype=np.float64)
@@ -218,4 +222,13 @@ def qkv_backward(x, w_norm, w_qkv, pos, gq, gk, gv, num_q_heads: int, num_kv_hea
     dw = np.sum(ga * x * r[:, None], axis=0)
     inner = np.sum(ga * w[None, :] * x, axis=1)
     dx = r[:, None] * w[None, :] * ga - (r ** 3 / H)[:, None] * x * inner[:, None]
+    if return_scales:
+        # root-sum-square of the terms each gradient element sums (see the docstring)
+        sq = lambda m: np.sqrt(np.maximum(m, 0.0))
+        scales = (r[:, None] * np.abs(w)[None, :] * sq((gy * gy) @ (W * W).T)
+                  + (r ** 3 / H)[:, None] * np.abs(x) * sq(np.sum((ga * w[None, :] * x) ** 2, axis=1))[:, None],
+                  sq(np.sum((ga * x * r[:, None]) ** 2, axis=0)),
+                  sq((a * a).T @ (gy * gy)),
+                  sq(np.sum(gy * gy, axis=0)) if with_bias else None)
+        return (dx, dw, dW, db), scales
     return dx, dw, dW, db

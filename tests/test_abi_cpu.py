@@ -87,6 +87,7 @@ def test_null_pointers_rejected():
     assert lib.qkv_forward(None, 4, *([None] * 8), None) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_rms_inv(None, 4, None, None, None) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_forward_kv_cache(None, 4, *([None] * 6), 16, None, None, None, None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_backward(None, 4, *([None] * 11), None) == qkv.QKV_ERR_INVALID_ARG
     v = ctypes.c_int32()
     assert lib.qkv_plan_variant(None, 4, ctypes.byref(v)) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_plan_destroy(None) == qkv.QKV_OK

@@ -27,6 +27,8 @@ EXPORTS = {
     "qkv_forward": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qkv_forward_kv_cache": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
                                             _vp, _vp, _vp, _vp]),
+    "qkv_backward": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _vp]),
     "qkv_swiglu_forward": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_double, _vp, _vp, _vp, _vp, _vp]),
     "qkv_rms_inv": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp]),
@@ -242,6 +244,30 @@ class Plan:
                                             _stream_handle(stream))
         _check(st, "qkv_forward_kv_cache")
         return q
+
+    def backward(self, x: torch.Tensor, w_norm: torch.Tensor, w_qkv: torch.Tensor, pos: torch.Tensor,
+                 dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor,
+                 stream: Optional[torch.cuda.Stream] = None):
+        """Gradients (dx, dw_norm, dw_qkv, dbias or None) of a loss whose gradients with
+        respect to Q, K, V are dq, dk, dv."""
+        T = x.shape[0]
+        H, N = self.hidden, self.n_q + 2 * self.n_kv
+        self._check_tensor(x, "x", (T, H), self.dtype)
+        self._check_tensor(w_norm, "w_norm", (H,), self.dtype)
+        self._check_tensor(w_qkv, "w_qkv", (H, N), self.dtype)
+        self._check_tensor(pos, "pos", (T,), torch.int32)
+        self._check_tensor(dq, "dq", (T, self.n_q), self.dtype)
+        self._check_tensor(dk, "dk", (T, self.n_kv), self.dtype)
+        self._check_tensor(dv, "dv", (T, self.n_kv), self.dtype)
+        dx = torch.empty((T, H), dtype=self.dtype, device=x.device)
+        dw = torch.empty((H,), dtype=self.dtype, device=x.device)
+        dW = torch.empty((H, N), dtype=self.dtype, device=x.device)
+        db = torch.empty((N,), dtype=self.dtype, device=x.device) if self.has_bias else None
+        st = self._lib.qkv_backward(self.handle, T, _ptr(x), _ptr(w_norm), _ptr(w_qkv), _ptr(pos), _ptr(dq),
+                                    _ptr(dk), _ptr(dv), _ptr(dx), _ptr(dw), _ptr(dW), _ptr(db),
+                                    _stream_handle(stream))
+        _check(st, "qkv_backward")
+        return dx, dw, dW, db
 
     def rms_inv(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:

@@ -30,6 +30,34 @@ struct ForwardArgs {
   bool bf16;
 };
 
+// Backward of the chain (see backward.hip): everything but the two GEMMs.
+struct BackwardArgs {
+  const void* x;
+  const void* w_norm;
+  const int32_t* pos;
+  const void* dq;
+  const void* dk;
+  const void* dv;
+  void* dx;
+  void* dw_norm;
+  void* dbias;             // nullptr when the plan has no bias
+  void* gy;                // scratch [T, N] plan dtype: unrotated upstream gradient
+  void* act;               // scratch [T, H] plan dtype: normalised activations
+  float* ga;               // scratch [T, H] fp32: gradient of the activations
+  float* inv_rms;          // scratch [T]
+  float* partial;          // scratch [kBackwardChunks, max(N, H)] fp32 column partial sums
+  const double* rev_freq;  // [d/2]
+  int T, H, N, Nq, Nkv, d;
+  float eps;
+  bool bf16;
+};
+constexpr int kBackwardChunks = 64;
+int backward_colsum_chunks(int T);
+// unrotate (gy), activations (a, r) and the bias gradient
+hipError_t launch_backward_pre_gemm(const BackwardArgs& b, hipStream_t stream);
+// dx and the norm-weight gradient, once ga = gy W^T is in b.ga
+hipError_t launch_backward_post_gemm(const BackwardArgs& b, hipStream_t stream);
+
 hipError_t launch_inv_rms(const void* x, float* inv_rms, int T, int H, float eps, bool bf16,
                           hipStream_t stream);
 hipError_t launch_generic(const ForwardArgs& a, hipStream_t stream);

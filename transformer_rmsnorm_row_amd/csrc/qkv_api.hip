@@ -8,6 +8,7 @@
 #include <unordered_set>
 
 #include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
 
 #include "qkv.h"
 #include "launch.h"
@@ -28,6 +29,12 @@ struct Plan {
   double* rev_freq;   // [head_dim/2]
   float* partials;    // decode partial sums
   uint32_t* counters; // decode arrival counters
+  // backward scratch, allocated by the first qkv_backward through the plan
+  void* bwd_gy;         // [max_tokens, N] plan dtype
+  void* bwd_act;        // [max_tokens, H] plan dtype
+  float* bwd_ga;        // [max_tokens, H] fp32
+  float* bwd_partial;   // [kBackwardChunks, max(N, H)] fp32
+  rocblas_handle blas;  // the two GEMMs of the backward
 };
 
 std::mutex g_mu;
@@ -80,10 +87,38 @@ void free_scratch(Plan* pl) {
   if (pl->rev_freq) (void)hipFree(pl->rev_freq);
   if (pl->partials) (void)hipFree(pl->partials);
   if (pl->counters) (void)hipFree(pl->counters);
+  if (pl->bwd_gy) (void)hipFree(pl->bwd_gy);
+  if (pl->bwd_act) (void)hipFree(pl->bwd_act);
+  if (pl->bwd_ga) (void)hipFree(pl->bwd_ga);
+  if (pl->bwd_partial) (void)hipFree(pl->bwd_partial);
+  if (pl->blas) (void)rocblas_destroy_handle(pl->blas);
   pl->inv_rms = nullptr;
   pl->rev_freq = nullptr;
   pl->partials = nullptr;
   pl->counters = nullptr;
+  pl->bwd_gy = pl->bwd_act = nullptr;
+  pl->bwd_ga = pl->bwd_partial = nullptr;
+  pl->blas = nullptr;
+}
+
+// First backward through a plan: its scratch and the GEMM library handle.
+qkv_status ensure_backward_scratch(Plan* pl) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (pl->blas) return QKV_OK;
+  const size_t T = (size_t)pl->desc.max_tokens, H = (size_t)pl->desc.hidden, N = (size_t)pl->N;
+  const size_t elem = pl->bf16 ? 2 : 4;
+  const size_t widest = N > H ? N : H;
+  bool ok = hipMalloc(&pl->bwd_gy, T * N * elem) == hipSuccess && hipMalloc(&pl->bwd_act, T * H * elem) == hipSuccess &&
+            hipMalloc(&pl->bwd_ga, T * H * sizeof(float)) == hipSuccess &&
+            hipMalloc(&pl->bwd_partial, (size_t)qkv::kBackwardChunks * widest * sizeof(float)) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    return QKV_ERR_OUT_OF_MEMORY;
+  }
+  rocblas_handle h = nullptr;
+  if (rocblas_create_handle(&h) != rocblas_status_success) return QKV_ERR_HIP;
+  pl->blas = h;
+  return QKV_OK;
 }
 
 int choose_variant(const Plan* pl, int64_t T) {
@@ -300,6 +335,70 @@ qkv_status qkv_swiglu_forward(int64_t num_tokens, int32_t hidden, int32_t interm
   a.bf16 = true;
   const hipError_t e = qkv::launch_swiglu(a, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
+}
+
+qkv_status qkv_backward(qkv_plan plan, int64_t num_tokens, const void* x, const void* w_norm, const void* w_qkv,
+                        const int32_t* pos, const void* dq, const void* dk, const void* dv, void* dx, void* dw_norm,
+                        void* dw_qkv, void* dbias, void* stream) {
+  Plan* pl = as_plan(plan);
+  if (!pl) return QKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return QKV_OK;
+  if (num_tokens < 0 || num_tokens > pl->desc.max_tokens) return QKV_ERR_INVALID_ARG;
+  if (!x || !w_norm || !w_qkv || !pos || !dq || !dk || !dv || !dx || !dw_norm || !dw_qkv)
+    return QKV_ERR_INVALID_ARG;
+  if ((dbias != nullptr) != (pl->desc.has_bias == 1)) return QKV_ERR_INVALID_ARG;
+  for (const void* p : {x, w_norm, w_qkv, dq, dk, dv, (const void*)dx, (const void*)dw_norm, (const void*)dw_qkv})
+    if (!aligned(p, 16)) return QKV_ERR_INVALID_ARG;
+  if (!aligned(pos, 4) || (dbias && !aligned(dbias, 16))) return QKV_ERR_INVALID_ARG;
+  qkv_status st = check_device(pl);
+  if (st != QKV_OK) return st;
+  st = ensure_backward_scratch(pl);
+  if (st != QKV_OK) return st;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  qkv::BackwardArgs b{};
+  b.x = x;
+  b.w_norm = w_norm;
+  b.pos = pos;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.dx = dx;
+  b.dw_norm = dw_norm;
+  b.dbias = dbias;
+  b.gy = pl->bwd_gy;
+  b.act = pl->bwd_act;
+  b.ga = pl->bwd_ga;
+  b.inv_rms = pl->inv_rms;
+  b.partial = pl->bwd_partial;
+  b.rev_freq = pl->rev_freq;
+  b.T = (int)num_tokens;
+  b.H = pl->desc.hidden;
+  b.N = pl->N;
+  b.Nq = pl->Nq;
+  b.Nkv = pl->Nkv;
+  b.d = pl->desc.head_dim;
+  b.eps = (float)pl->desc.eps;
+  b.bf16 = pl->bf16;
+  if (qkv::launch_backward_pre_gemm(b, s) != hipSuccess) return QKV_ERR_HIP;
+
+  // Row-major [T, N] gy is the column-major N x T matrix gy^T (leading dimension N),
+  // and likewise for a, W and the outputs.
+  //   dW (row-major [H, N])  = a^T gy   <=>  (column-major N x H) = gy^T (N x T) * a (T x H)
+  //   ga (row-major [T, H])  = gy W^T   <=>  (column-major H x T) = W (H x N) * gy^T (N x T)
+  if (rocblas_set_stream(pl->blas, s) != rocblas_status_success) return QKV_ERR_HIP;
+  const rocblas_datatype io = pl->bf16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+  const float one = 1.0f, zero = 0.0f;
+  const int T = b.T, H = b.H, N = b.N;
+  rocblas_status rs = rocblas_gemm_ex(pl->blas, rocblas_operation_none, rocblas_operation_transpose, N, H, T, &one,
+                                      b.gy, io, N, b.act, io, H, &zero, dw_qkv, io, N, dw_qkv, io, N,
+                                      rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+  if (rs != rocblas_status_success) return QKV_ERR_HIP;
+  rs = rocblas_gemm_ex(pl->blas, rocblas_operation_transpose, rocblas_operation_none, H, T, N, &one, w_qkv, io, N,
+                       b.gy, io, N, &zero, b.ga, rocblas_datatype_f32_r, H, b.ga, rocblas_datatype_f32_r, H,
+                       rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+  if (rs != rocblas_status_success) return QKV_ERR_HIP;
+  return qkv::launch_backward_post_gemm(b, s) == hipSuccess ? QKV_OK : QKV_ERR_HIP;
 }
 
 const char* qkv_status_string(qkv_status status) {

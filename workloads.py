@@ -166,3 +166,14 @@ def make_mlp_inputs(wl: MlpWorkload, seed: int = 6000) -> dict:
     w_gate_up = (torch.randn(H, 2 * inter, generator=_gen(seed + 2), dtype=torch.float32) * 0.02).to(torch.bfloat16)
     w_norm = (1.0 + 0.1 * torch.randn(H, generator=_gen(seed + 3), dtype=torch.float32)).to(torch.bfloat16)
     return {"x": x, "w_norm": w_norm, "w_gate_up": w_gate_up}
+
+
+def make_grads(wl: Workload, seed: Optional[int] = None) -> dict:
+    """Host tensors of upstream gradients for Q, K, V (N(0,1), the workload's dtype)."""
+    base = 1000 * wl.cid + 500 if seed is None else seed
+    T, dt = wl.tokens, wl.torch_dtype
+    return {
+        "dq": torch.randn(T, wl.n_q, generator=_gen(base + 1), dtype=torch.float32).to(dt),
+        "dk": torch.randn(T, wl.n_kv, generator=_gen(base + 2), dtype=torch.float32).to(dt),
+        "dv": torch.randn(T, wl.n_kv, generator=_gen(base + 3), dtype=torch.float32).to(dt),
+    }
