@@ -290,43 +290,57 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
+  // A bare s_barrier: this wave's LDS reads and loads may still be in flight.
+  auto raw_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   // One step t (t % 4 == P).  Waves 0-3 run the memory phase of step t while waves
   // 4-7 run the compute phase of step t - 1, and the other way round one phase later.
   // Memory phase: read this wave's fragments of step t (activation slot t % 2, weight
   // slot t % 4), issue x(t + 2) into register set t % 2 and W(t + 3) into weight slot
-  // (t + 3) % 4, and wait until x(t + 1) has landed.  Per wave the vector-memory order
-  // is ..., W(t + 1), x(t + 1), W(t + 2), x(t + 2), W(t + 3), so that wait is
-  // vmcnt(7), and it also covers W(t + 1).  Compute phase: the MFMAs of step t and the
-  // conversion of x(t + 1) into activation slot (t + 1) % 2.
+  // (t + 3) % 4, and wait until this wave's part of W(t + 1) has landed.  Per wave the
+  // vector-memory order is ..., W(t + 1), x(t + 1), W(t + 2), x(t + 2), W(t + 3), so
+  // that wait is vmcnt(10).  The phase ends at a bare barrier: its fragment reads may
+  // still be in flight, since nothing written in the next phase (the other group's
+  // weight DMA into slot (t - 1) % 4, this group's conversion into activation slot
+  // (t + 1) % 2) aliases them.  Compute phase: wait for x(t + 1) (vmcnt(7)), the MFMAs
+  // of step t and the conversion of x(t + 1) into activation slot (t + 1) % 2, closed
+  // by a full barrier so the converted rows are in LDS before this group reads them.
   // Slot reuse is safe: weight slot (t + 3) % 4 held step t - 1, which both groups
   // read in memory phases that ended before this phase began; activation slot
   // (t + 1) % 2 held step t - 1 of this group's rows, read in its previous memory
   // phase; register set t % 2 was converted in the previous compute phase.  Every wave
-  // has its own loads of step t + 1 complete before the barrier that ends its memory
-  // phase t, and the first reads of step t + 1 come after that barrier.
+  // has its part of W(t + 1) complete before the barrier that ends its memory phase t,
+  // and the first reads of W(t + 1) come after that barrier.
   // Mode: 0 issue x(t + 2) and W(t + 3); 1 issue x(t + 2) only (t = K/32 - 3);
-  // 2 issue nothing and wait for everything (t = K/32 - 2); 3 the last step.
+  // 2 issue nothing and wait for everything by its compute phase (t = K/32 - 2);
+  // 3 the last step.
   auto step = [&](auto Pc, int t, auto ModeC) {
     constexpr int P = decltype(Pc)::value;
     constexpr int kMode = decltype(ModeC)::value;
     constexpr bool kLast = kMode == 3;
     read_frags(P & 1, P);
-    if constexpr (!kLast) {
-      if constexpr (kMode == 0) {
-        issue_x(t + 2, P & 1);
-        issue_w(t + 3, (P + 3) & 3);
-        wait_vmcnt<2 * kWOps + kXOps>();
-      } else if constexpr (kMode == 1) {
-        issue_x(t + 2, P & 1);
-        wait_vmcnt<kWOps + kXOps>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      tie_set((P + 1) & 1);
+    // memory phase: only this wave's part of W(t + 1) has to be complete at its end
+    if constexpr (kMode == 0) {
+      issue_x(t + 2, P & 1);
+      issue_w(t + 3, (P + 3) & 3);
+      wait_vmcnt<2 * kWOps + 2 * kXOps>();
+    } else if constexpr (kMode == 1) {
+      issue_x(t + 2, P & 1);
+      wait_vmcnt<kWOps + 2 * kXOps>();
+    } else if constexpr (kMode == 2) {
+      wait_vmcnt<kXOps>();
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    barrier();
+    raw_barrier();
+    // compute phase: x(t + 1) in registers before its conversion; the compiler waits
+    // for each fragment register before the MFMA that reads it
+    if constexpr (kMode == 0) wait_vmcnt<2 * kWOps + kXOps>();
+    else if constexpr (kMode == 1) wait_vmcnt<kWOps + kXOps>();
+    else if constexpr (kMode == 2) wait_vmcnt<0>();
+    if constexpr (!kLast) tie_set((P + 1) & 1);
     compute((P + 1) & 1, (P + 1) & 1, !kLast);
     barrier();
   };
