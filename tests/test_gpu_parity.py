@@ -110,6 +110,20 @@ def test_head_shapes(nq, nkv, d, dtype):
     P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL[dtype], wl.name)
 
 
+@pytest.mark.parametrize("nq,nkv,d", [(8, 2, 64), (4, 1, 256), (16, 4, 64), (2, 1, 256)])
+def test_prefill_head_sizes(nq, nkv, d):
+    """Head sizes 64 and 256 on the MFMA prefill kernel (rotation partners d/2 apart,
+    so a wave's two column blocks sit 32 or 128 columns apart), with bias and a ragged
+    last row tile."""
+    wl = workloads.Workload(12, f"prefill_d{d}_{nq}x{nkv}", 1, 300, 384, nq, nkv, d, True, 1e4, 1e-6, "bf16",
+                            "per_seq")
+    inp = workloads.make_inputs(wl, seed=7 * d + nq)
+    with qkv.Plan.for_workload(wl) as plan:
+        assert plan.variant(wl.tokens) == "prefill"
+        got = run(plan, inp)
+    print(P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], wl.name))
+
+
 @pytest.mark.parametrize("hidden", [128, 384, 640, 1152, 5120, 8192])
 def test_prefill_hidden_sizes(hidden):
     """K extents that exercise the prefill kernel's loop structure: H = 128 runs only

@@ -112,7 +112,16 @@ using Int = std::integral_constant<int, P>;
 // rotary embedding, Q/K/V stores) and the gated MLP (SiLU(gate) * up).
 constexpr int kEpiQkv = 0, kEpiSwiglu = 1;
 
-template <int kEpi>
+// Tile column of the first of a wave's two 32-column blocks for head size kD; the
+// second block, at + kD/2, holds the rotation partners of the first.  Each 32-column
+// block of the tile belongs to exactly one wave of a row group.
+template <int kD>
+__device__ __forceinline__ int pair_block(int slot) {
+  static_assert(kD == 64 || kD == 128 || kD == 256, "head sizes of the MFMA kernel");
+  return kD == 128 ? 128 * (slot >> 1) + 32 * (slot & 1) : (kD == 256 ? 32 * slot : 64 * slot);
+}
+
+template <int kEpi, int kD>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
 
@@ -134,8 +143,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int grp = wave >> 2, slot = wave & 3;
-  const int head = slot >> 1;          // which of the tile's two heads
-  const int c0 = (slot & 1) * 32;      // first rotation-pair index of this wave
+  const int head = slot >> 1;          // which 128-column half of the tile this wave stores
+  const int blk = pair_block<kD>(slot);  // tile column of the wave's first block
+  const int c0 = blk % kD;             // first rotation-pair index of this wave
   const int H = a.H, N = a.N, T = a.T;
   const uint32_t fl = lane & 31, fh = lane >> 5;
 
@@ -184,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const uint32_t krow = 8u * (tg >> 1) + (tj >> 2);
-    const uint32_t col = 128u * head + c0 + 64u * cb + 16u * (tg & 1) + 4u * (tj & 3);
+    const uint32_t col = (uint32_t)(blk + (kD / 2) * cb) + 16u * (tg & 1) + 4u * (tj & 3);
     b_roff[cb] = kWBase + krow * 512u + wchunk(krow, col >> 3) * 16u + (col & 7u) * 2u;
   }
 
@@ -352,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   // Range-checked buffer loads need no branch (rows past T read position 0, a plan
   // without bias reads 0 through an empty range), so nothing waits for them before
   // their first use in the epilogue.
-  const int hcol = n0 + head * 128;  // first column of this wave's head
+  const int hcol = n0 + head * 128;  // first column of the 128-column half this wave stores
   int32_t pos_pref = 0, slot_pref = -1;
   uint16_t braw[2] = {0, 0};
   uint64_t rev_bits = 0;
@@ -364,9 +374,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     const auto b_rsrc = make_rsrc(a.bias ? a.bias : a.w, a.bias ? (uint32_t)N * 2u : 0u);
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
-      braw[cb] = __builtin_amdgcn_raw_buffer_load_b16(b_rsrc, (int)((uint32_t)(hcol + c0 + cb * 64 + fl) * 2u), 0, 0);
-    rev_bits = __builtin_bit_cast(
-        uint64_t, __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(a.rev_freq, 64u * 8u), (int)((uint32_t)(c0 + fl) * 8u), 0, 0));
+      braw[cb] = __builtin_amdgcn_raw_buffer_load_b16(b_rsrc, (int)((uint32_t)(n0 + blk + (kD / 2) * cb + fl) * 2u), 0, 0);
+    rev_bits = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(a.rev_freq, (kD / 2) * 8u),
+                                                                                 (int)((uint32_t)(c0 + fl) * 8u), 0, 0));
   }
   // prologue: W(0..2) and x(0..1) issued, x(0) converted into activation slot 0
   issue_w(0, 0);
@@ -474,7 +484,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     // ---- epilogue: scale, bias, rotate, stage as bf16, store
     const float bcol[2] = {bf16_to_f32(braw[0]), bf16_to_f32(braw[1])};
     const double rev = __builtin_bit_cast(double, rev_bits);
-    const bool rotate = hcol < a.Nq + a.Nkv;
+    // (the head's tensor: both blocks of the wave and the half it stores lie in one of
+    // Q, K, V, whose column counts are multiples of 128 and of the head size)
+    const bool rotate = n0 + blk < a.Nq + a.Nkv;
     void* out;
     uint32_t width, ocol;
     if (hcol < a.Nq) {
@@ -486,6 +498,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     }
 
     uint8_t* stage = smem + (grp * 2 + head) * kBlockStage;
+    // block cb goes to the stage of its 128-column half, at its column within that half
+    uint8_t* const stg[2] = {smem + (grp * 2 + blk / 128) * kBlockStage,
+                             smem + (grp * 2 + (blk + kD / 2) / 128) * kBlockStage};
+    const int scol[2] = {blk % 128 + (int)fl, (blk + kD / 2) % 128 + (int)fl};
     // one instantiation per case, so the uniform test is not repeated (as a branch)
     // around every element and independent elements can overlap
     auto scale_rotate_stage = [&](auto RotC) {
@@ -508,9 +524,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
               y0 = u0 * c - v0 * s;
               y1 = v0 * c + u0 * s;
             }
-            uint16_t* srow = reinterpret_cast<uint16_t*>(stage + (rbase + rr) * kStagePitch);
-            srow[c0 + fl] = f32_to_bf16(y0);
-            srow[c0 + 64 + fl] = f32_to_bf16(y1);
+            reinterpret_cast<uint16_t*>(stg[0] + (rbase + rr) * kStagePitch)[scol[0]] = f32_to_bf16(y0);
+            reinterpret_cast<uint16_t*>(stg[1] + (rbase + rr) * kStagePitch)[scol[1]] = f32_to_bf16(y1);
           }
         }
       }
@@ -544,12 +559,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
 }  // namespace
 
 bool prefill_supports(int H, int N, int Nq, int Nkv, int d) {
-  return d == 128 && H % (4 * BK) == 0 && N % BN == 0 && Nq % 128 == 0 && Nkv % 128 == 0;
+  return (d == 64 || d == 128 || d == 256) && H % (4 * BK) == 0 && N % BN == 0 && Nq % 128 == 0 &&
+         Nkv % 128 == 0 && Nq % d == 0 && Nkv % d == 0;
 }
 
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream) {
   const int tiles_m = (a.T + BM - 1) / BM, tiles_n = a.N / BN;
-  prefill_kernel<kEpiQkv><<<dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
+  const dim3 grid(tiles_m * tiles_n), block(kThreads);
+  if (a.d == 64)
+    prefill_kernel<kEpiQkv, 64><<<grid, block, 0, stream>>>(a, tiles_m, tiles_n);
+  else if (a.d == 256)
+    prefill_kernel<kEpiQkv, 256><<<grid, block, 0, stream>>>(a, tiles_m, tiles_n);
+  else
+    prefill_kernel<kEpiQkv, 128><<<grid, block, 0, stream>>>(a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -558,7 +580,7 @@ bool swiglu_supports(int H, int I) { return H % (4 * BK) == 0 && I % 128 == 0; }
 hipError_t launch_swiglu(const ForwardArgs& a, hipStream_t stream) {
   // a.N = 2I columns of [gate | up]; the output (a.q) is [T, I]
   const int tiles_m = (a.T + BM - 1) / BM, tiles_n = a.N / BN;
-  prefill_kernel<kEpiSwiglu><<<dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
+  prefill_kernel<kEpiSwiglu, 128><<<dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
