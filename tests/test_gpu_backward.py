@@ -68,6 +68,10 @@ CASES = {
     "bf16_bias_ragged": (workloads.WORKLOADS[5], dict(batch=1, seq=300, hidden=384, num_q_heads=4, num_kv_heads=2)),
     "gqa_1024": (workloads.WORKLOADS[3], dict(batch=1, seq=1024)),
     "decode_shape": (workloads.WORKLOADS[4], {}),
+    "bf16_d64": (workloads.WORKLOADS[2], dict(batch=2, seq=100, hidden=256, num_q_heads=8, num_kv_heads=2,
+                                               head_dim=64)),
+    "fp32_d256": (workloads.WORKLOADS[1], dict(batch=1, seq=40, hidden=128, num_q_heads=2, num_kv_heads=1,
+                                                head_dim=256)),
 }
 
 
