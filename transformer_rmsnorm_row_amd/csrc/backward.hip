@@ -36,6 +36,80 @@ __device__ __forceinline__ void st(void* p, size_t i, float v) {
     ((float*)p)[i] = v;
 }
 
+// 8 consecutive elements of a row as fp32 (one 16-byte load for bf16, two for fp32)
+// and back.  Callers keep the offsets multiples of 8 elements (H % 8 == 0 and d % 16
+// == 0 where used).
+template <bool BF16>
+__device__ __forceinline__ void ld8(const void* p, size_t i, float (&v)[8]) {
+  if constexpr (BF16) {
+    const u32x4 r = *reinterpret_cast<const u32x4*>((const uint16_t*)p + i);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[2 * c] = bf16_lo(r[c]);
+      v[2 * c + 1] = bf16_hi(r[c]);
+    }
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>((const float*)p + i);
+    const f32x4 b = *reinterpret_cast<const f32x4*>((const float*)p + i + 4);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[c] = a[c];
+      v[4 + c] = b[c];
+    }
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void st8(void* p, size_t i, const float (&v)[8]) {
+  if constexpr (BF16) {
+    u32x4 r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r[c] = pack_bf16x2(v[2 * c], v[2 * c + 1]);
+    *reinterpret_cast<u32x4*>((uint16_t*)p + i) = r;
+  } else {
+    *reinterpret_cast<f32x4*>((float*)p + i) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>((float*)p + i + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
+// One thread per (token, 8 consecutive rotation pairs of one head): 16-byte loads of
+// the u and v halves.  Used when d/2 is a multiple of 8.
+template <bool BF16>
+__global__ __launch_bounds__(256) void unrotate8_kernel(BackwardArgs b) {
+  const int half = b.d / 2, units = b.N / 16;  // 8-pair groups per token
+  const size_t total = (size_t)b.T * units;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+    const int t = (int)(e / units), g = (int)(e % units);
+    const int p0 = g * 8;                                 // first pair of the group
+    const int c = (p0 / half) * b.d + (p0 % half);        // its first column
+    const void* src;
+    int width, oc;
+    if (c < b.Nq) {
+      src = b.dq; width = b.Nq; oc = c;
+    } else if (c < b.Nq + b.Nkv) {
+      src = b.dk; width = b.Nkv; oc = c - b.Nq;
+    } else {
+      src = b.dv; width = b.Nkv; oc = c - b.Nq - b.Nkv;
+    }
+    float gu[8], gv[8];
+    ld8<BF16>(src, (size_t)t * width + oc, gu);
+    ld8<BF16>(src, (size_t)t * width + oc + half, gv);
+    if (c < b.Nq + b.Nkv) {
+      const int i0 = p0 % half;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float cs, sn;
+        rope_cos_sin(b.pos[t], b.rev_freq[i0 + j], cs, sn);
+        const float u = gu[j], v = gv[j];
+        gu[j] = u * cs + v * sn;
+        gv[j] = v * cs - u * sn;
+      }
+    }
+    st8<BF16>(b.gy, (size_t)t * b.N + c, gu);
+    st8<BF16>(b.gy, (size_t)t * b.N + c + half, gv);
+  }
+}
+
 // One thread per (token, rotation pair); pairs enumerate features i < d/2 of every
 // head of Q, K and V (V pairs are copied unrotated).
 template <bool BF16>
@@ -75,13 +149,22 @@ __global__ __launch_bounds__(256) void activations_kernel(BackwardArgs b) {
   if (t >= b.T) return;
   const size_t row = (size_t)t * b.H;
   float ss = 0.f;
-  for (int k = lane; k < b.H; k += 64) {
-    const float v = ld<BF16>(b.x, row + k);
-    ss = fmaf(v, v, ss);
+  for (int k = lane * 8; k < b.H; k += 512) {
+    float v[8];
+    ld8<BF16>(b.x, row + k, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
   }
   const float r = rsqrtf(wave_sum(ss) / (float)b.H + b.eps);
   if (lane == 0) b.inv_rms[t] = r;
-  for (int k = lane; k < b.H; k += 64) st<BF16>(b.act, row + k, ld<BF16>(b.x, row + k) * r * ld<BF16>(b.w_norm, k));
+  for (int k = lane * 8; k < b.H; k += 512) {
+    float v[8], w[8];
+    ld8<BF16>(b.x, row + k, v);
+    ld8<BF16>(b.w_norm, k, w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = v[j] * r * w[j];
+    st8<BF16>(b.act, row + k, v);
+  }
 }
 
 // One wave per token: dx from ga (fp32), x, w and r.
@@ -92,12 +175,26 @@ __global__ __launch_bounds__(256) void norm_grad_kernel(BackwardArgs b) {
   if (t >= b.T) return;
   const size_t row = (size_t)t * b.H;
   float inner = 0.f;
-  for (int k = lane; k < b.H; k += 64) inner = fmaf(b.ga[row + k] * ld<BF16>(b.w_norm, k), ld<BF16>(b.x, row + k), inner);
+  for (int k = lane * 8; k < b.H; k += 512) {
+    float g[8], w[8], x[8];
+    ld8<false>(b.ga, row + k, g);
+    ld8<BF16>(b.w_norm, k, w);
+    ld8<BF16>(b.x, row + k, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) inner = fmaf(g[j] * w[j], x[j], inner);
+  }
   inner = wave_sum(inner);
   const float r = b.inv_rms[t];
   const float c2 = r * r * r / (float)b.H * inner;
-  for (int k = lane; k < b.H; k += 64)
-    st<BF16>(b.dx, row + k, r * ld<BF16>(b.w_norm, k) * b.ga[row + k] - c2 * ld<BF16>(b.x, row + k));
+  for (int k = lane * 8; k < b.H; k += 512) {
+    float g[8], w[8], x[8];
+    ld8<false>(b.ga, row + k, g);
+    ld8<BF16>(b.w_norm, k, w);
+    ld8<BF16>(b.x, row + k, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) g[j] = r * w[j] * g[j] - c2 * x[j];
+    st8<BF16>(b.dx, row + k, g);
+  }
 }
 
 // Column sums over tokens, pass 1: block (column group, token chunk) -> fp32 partial.
@@ -138,9 +235,15 @@ hipError_t colsum(const BackwardArgs& b, int ncols, void* out, hipStream_t strea
 
 template <bool BF16>
 hipError_t pre_gemm(const BackwardArgs& b, hipStream_t stream) {
-  const size_t total = (size_t)b.T * (b.N / 2);
-  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
-  unrotate_kernel<BF16><<<dim3(blocks), dim3(256), 0, stream>>>(b);
+  if ((b.d / 2) % 8 == 0) {
+    const size_t total = (size_t)b.T * (b.N / 16);
+    const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+    unrotate8_kernel<BF16><<<dim3(blocks), dim3(256), 0, stream>>>(b);
+  } else {
+    const size_t total = (size_t)b.T * (b.N / 2);
+    const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+    unrotate_kernel<BF16><<<dim3(blocks), dim3(256), 0, stream>>>(b);
+  }
   activations_kernel<BF16><<<dim3((b.T + 3) / 4), dim3(256), 0, stream>>>(b);
   if (b.dbias) return colsum<BF16, 0>(b, b.N, b.dbias, stream);
   return hipGetLastError();
