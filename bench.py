@@ -16,6 +16,11 @@ line carries:
                 HBM traffic measured by rocprofv3 counters when it is current;
   decode        the 64-token decode step streaming its weight from HBM (8 weight
                 copies rotated so the 256 MB last-level cache cannot hold them);
+  other_workloads  every other forward workload (tiny fp32, Llama-3-8B GQA prefill,
+                the decode step warm, Qwen-7B prefill with bias) at full size;
+  prefill_zero_weight  the headline forward with an all-zero weight, a labelled
+                diagnostic: how much of the prefill time is the clock lost to the
+                matrix cores' power draw on random operands;
   cpu_baseline  the fp64 CPU oracle on the host cores, one full forward of the
                 same workload (a reported baseline, not a target).
 """
@@ -303,6 +308,51 @@ def swiglu_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
             "algorithmic_bytes": wl.algorithmic_bytes()}
 
 
+def other_workloads_leg(qkv, workloads, skip: str, steps: int = 30, warmup: int = 5):
+    """Every other forward workload at its full size, back-to-back calls timed with HIP
+    events on the current stream: prefill ones against the bf16 (or fp32) matrix peak,
+    the decode step against HBM (warm last-level cache here; the decode leg streams it
+    cold)."""
+    import torch
+    res = {}
+    for wl in workloads.WORKLOADS.values():
+        if wl.name == skip:
+            continue
+        inp = workloads.make_inputs(wl)
+        bufs = device_inputs(wl, inp)
+        with qkv.Plan.for_workload(wl) as plan:
+            variant = plan.variant(wl.tokens)
+            _, sec = time_forward(plan, bufs, steps, warmup)
+        flops, nbytes = wl.flops(), wl.algorithmic_bytes()
+        entry = {"tokens": wl.tokens, "variant": variant, "us": round(sec * 1e6, 2),
+                 "tokens_per_s": round(wl.tokens / sec, 1), "tflops": round(flops / sec / 1e12, 3),
+                 "hbm_GBps": round(nbytes / sec / 1e9, 1)}
+        if wl.tokens > 256:
+            peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+            entry["mfma_frac"] = round(flops / sec / 1e12 / peak, 4)
+        elif wl.dtype == "bf16":
+            entry["timing"] = "weight warm in the last-level cache (see the decode object for HBM-cold)"
+        else:
+            entry["timing"] = "launch-bound (two launches: row reduction and fp32 kernel)"
+        res[wl.name] = entry
+        del bufs
+        torch.cuda.empty_cache()
+    return res
+
+
+def zero_weight_leg(plan, bufs, steps: int = 30, warmup: int = 5):
+    """The same forward with an all-zero weight: identical instructions and memory
+    traffic, but matrix-core operands that never toggle.  The ratio to the seeded
+    weight's time shows how much of the prefill time is set by the power the matrix
+    cores draw on random data (the shader clock is managed down under that load)."""
+    import torch
+    x, w, W, b, pos, q, k, v = bufs
+    Wz = torch.zeros_like(W)
+    _, sec = time_forward(plan, (x, w, Wz, b, pos, q, k, v), steps, warmup)
+    del Wz
+    return sec
+
+
 def cpu_baseline_leg(wl, inp):
     """The fp64 oracle, as it stands, on the host cores: one full forward."""
     import numpy as np
@@ -340,7 +390,11 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the key/value-cache and gated-MLP legs (time only the workload's own forward)")
+                    help="skip the key/value-cache, gated-MLP, backward, other-workload and zero-weight legs "
+                         "(time only the workload's own forward)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cache-flushed per-call prefill timing (so a profiled run holds only the "
+                         "timed back-to-back forwards)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (steps times), to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings against a known byte count")
@@ -374,9 +428,12 @@ def main() -> int:
           f"steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     wall, kernel_s = time_forward(plan, bufs, args.steps, args.warmup)
     cold = None
-    if wl.tokens > 256:
+    if wl.tokens > 256 and not args.no_cold:
         cold = time_forward_cold(plan, bufs)
     cache_s = None if args.no_extra else time_forward_kv_cache(qkv, wl, plan, bufs, args.steps, args.warmup)
+    zero_s = None
+    if not args.no_extra and wl.tokens > 256 and wl.dtype == "bf16":
+        zero_s = zero_weight_leg(plan, bufs)
     plan.close()
 
     flops = wl.flops()
@@ -415,6 +472,11 @@ def main() -> int:
                            "time_vs_dense": round(cache_s / kernel_s, 4),
                            "cache": "K and V rows written to slot = sequence's first row + position mod C "
                                     "of [batch x C, kv_heads*head_dim] caches, C = max(4096, seq_len)"}
+    if zero_s is not None:
+        out["prefill_zero_weight"] = {
+            "us": round(zero_s * 1e6, 2), "time_vs_seeded": round(zero_s / kernel_s, 4),
+            "note": "same kernel and traffic with an all-zero weight (operands that do not toggle): the seeded "
+                    "N(0,0.02) weight's extra time is the clock the matrix cores' power draw costs"}
     if cold:
         pct = lambda p: cold[min(len(cold) - 1, int(round(p * (len(cold) - 1))))]
         med = pct(0.5)
@@ -431,6 +493,10 @@ def main() -> int:
         out["swiglu"] = swiglu_leg(qkv, workloads)
         print("[bench] backward leg", file=sys.stderr, flush=True)
         out["backward"] = backward_leg(qkv, workloads, wl, bufs)
+        del bufs
+        torch.cuda.empty_cache()
+        print("[bench] other workloads leg", file=sys.stderr, flush=True)
+        out["other_workloads"] = other_workloads_leg(qkv, workloads, skip=wl.name)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline leg", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_leg(wl, inp)
