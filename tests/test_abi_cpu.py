@@ -147,3 +147,24 @@ def test_swiglu_arguments_rejected_before_any_hip_call():
     assert lib.qkv_swiglu_forward(4, 4000, 11008, bf16, 1e-6, *ok_ptrs, None) == qkv.QKV_ERR_UNSUPPORTED
     assert lib.qkv_swiglu_forward(4, 4096, 11000, bf16, 1e-6, *ok_ptrs, None) == qkv.QKV_ERR_UNSUPPORTED
     assert lib.qkv_swiglu_forward(1 << 20, 4096, 11008, bf16, 1e-6, *ok_ptrs, None) == qkv.QKV_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("shape", [
+    dict(hidden=4096, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype=1),    # widest row: N = 6144
+    dict(hidden=4096, num_q_heads=32, num_kv_heads=32, head_dim=128, dtype=1),   # N = 12288
+    dict(hidden=8192, num_q_heads=8, num_kv_heads=8, head_dim=128, dtype=0),     # widest row: x, fp32
+])
+def test_token_limit_is_exact(shape):
+    """Every kernel addresses a tensor with 32-bit byte offsets, so a plan's token count
+    times its widest row (x, or the projection's N columns) times the element size must
+    stay below 2^31: the first count at that bound is refused before any HIP call, and
+    the count below it gets past validation."""
+    elem = 2 if shape["dtype"] == 1 else 4
+    n = (shape["num_q_heads"] + 2 * shape["num_kv_heads"]) * shape["head_dim"]
+    limit = (1 << 31) // (max(n, shape["hidden"]) * elem)
+    st, h = _create(max_tokens=limit, **shape)
+    assert st == qkv.QKV_ERR_UNSUPPORTED and h.value is None
+    st, h = _create(max_tokens=limit - 1, **shape)
+    assert st in (qkv.QKV_OK, qkv.QKV_ERR_HIP)
+    if st == qkv.QKV_OK:
+        assert qkv.load_library().qkv_plan_destroy(h) == qkv.QKV_OK

@@ -68,6 +68,33 @@ def test_prefill_full_size_sampled_rows(cid):
     print(P.assert_parity(got, ref, P.TOL["bf16"], wl.name, rows=rows))
 
 
+def test_prefill_largest_plan():
+    """The largest token count a plan of the Llama-3-8B GQA shape accepts: kernels use
+    32-bit byte offsets, so tokens x widest row (6144 columns) x 2 bytes stays below
+    2^31.  One forward over 174761 tokens (682 full 256-row tiles and a ragged one,
+    16392 workgroups), sampled rows against the oracle; one token more is refused."""
+    base = workloads.WORKLOADS[3]
+    limit = (1 << 31) // (base.n_total * 2)
+    wl = base.with_tokens(1, limit - 1)
+    with pytest.raises(qkv.QKVError) as err:
+        qkv.Plan.for_workload(wl, max_tokens=limit)
+    assert err.value.status == qkv.QKV_ERR_UNSUPPORTED
+    inp = workloads.make_inputs(wl, seed=4242)
+    print(f"largest plan: T={wl.tokens}", flush=True)
+    with qkv.Plan.for_workload(wl) as plan:
+        assert plan.variant(wl.tokens) == "prefill"
+        got = run(plan, inp)
+    rows = P.sample_rows(wl.tokens, 256, seed=11)
+    idx = torch.as_tensor(rows, device=DEV)
+    got_rows = tuple(t.index_select(0, idx) for t in got)
+    for t in got_rows:
+        assert torch.isfinite(t).all(), "non-finite output"
+    # tokens are independent: the oracle over the sampled rows alone gives their outputs
+    sub = dict(inp, x=inp["x"][rows], pos=inp["pos"][rows])
+    ref = P.oracle_forward(wl, sub)
+    print(P.assert_parity(got_rows, ref, P.TOL["bf16"], "largest plan"))
+
+
 # ---------------------------------------------------------------- ragged sizes, full comparison
 
 MEDIUM = [
