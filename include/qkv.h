@@ -70,7 +70,8 @@ typedef enum qkv_dtype {
 typedef enum qkv_variant {
   QKV_VARIANT_GENERIC = 0,  /* fp32 FMA tiles: any supported shape, both dtypes        */
   QKV_VARIANT_PREFILL = 1,  /* bf16 MFMA GEMM, norm-on-load, rotary epilogue           */
-  QKV_VARIANT_DECODE = 2    /* bf16 MFMA weight-streaming kernel for small token counts */
+  QKV_VARIANT_DECODE = 2    /* bf16 MFMA weight-streaming kernel for small token counts:
+                               up to 256 tokens, one launch per 64-token chunk          */
 } qkv_variant;
 
 typedef struct qkv_plan_s* qkv_plan;
@@ -201,7 +202,10 @@ qkv_status qkv_swiglu_forward(int64_t num_tokens, int32_t hidden, int32_t interm
                               const void* x, const void* w_norm, const void* w_gate_up,
                               void* out, void* stream);
 
-/* Which variant a forward of num_tokens tokens runs on, in *variant (a qkv_variant).
+/* Which variant a forward of num_tokens tokens runs on, in *variant (a qkv_variant):
+ * bf16 plans of a shape the decode kernel supports take it up to 256 tokens (as
+ * consecutive launches of up to 64 tokens, queued in order on the forward's stream),
+ * other bf16 plans of a supported shape the prefill kernel, everything else generic.
  * Host-only; returns QKV_ERR_INVALID_ARG for a bad plan or num_tokens out of range. */
 qkv_status qkv_plan_variant(qkv_plan plan, int64_t num_tokens, int32_t* variant);
 

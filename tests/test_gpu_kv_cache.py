@@ -59,6 +59,7 @@ CASES = {
     "generic": (workloads.WORKLOADS[1], {}, 40),
     "prefill": (workloads.WORKLOADS[3], dict(batch=1, seq=300, hidden=1152, num_q_heads=4, num_kv_heads=2), 700),
     "decode": (workloads.WORKLOADS[4], {}, 200),
+    "decode_chunks": (workloads.WORKLOADS[4], dict(batch=150), 400),
     "prefill_d256": (workloads.WORKLOADS[3], dict(batch=1, seq=300, hidden=384, num_q_heads=4, num_kv_heads=2,
                                                   head_dim=256), 650),
     "prefill_d64": (workloads.WORKLOADS[3], dict(batch=1, seq=300, hidden=384, num_q_heads=8, num_kv_heads=2,

@@ -300,6 +300,33 @@ def test_decode_shapes(hidden, nq, nkv, bias):
     P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], wl.name)
 
 
+@pytest.mark.parametrize("T", [65, 100, 128, 191, 256])
+def test_decode_in_chunks(T):
+    """65 to 256 tokens run the decode kernel once per 64-token chunk (fewer than a
+    prefill tile's 256 rows would leave most compute units idle); full comparison with
+    the oracle, and each chunk's rows bit for bit equal to a forward of that chunk alone."""
+    wl = workloads.WORKLOADS[4].with_tokens(T, 1)
+    inp = workloads.make_inputs(wl, seed=700 + T)
+    with qkv.Plan.for_workload(wl) as plan:
+        assert plan.variant(T) == "decode"
+        got = run(plan, inp)
+        P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], f"decode chunks T={T}")
+        for t0 in range(0, T, 64):
+            part = {k: (v[t0:t0 + 64] if k in ("x", "pos") else v) for k, v in inp.items()}
+            one = run(plan, part)
+            for name, g, o in zip("QKV", got, one):
+                assert torch.equal(g[t0:t0 + 64], o), f"{name}: chunk at {t0} differs from its own forward"
+
+
+def test_decode_chunk_boundary():
+    """The decode kernel serves up to 256 tokens of a plan; 257 go to the prefill kernel."""
+    wl = workloads.WORKLOADS[4].with_tokens(257, 1)
+    with qkv.Plan.for_workload(wl) as plan:
+        assert plan.variant(256) == "decode"
+        assert plan.variant(257) == "prefill"
+        assert plan.variant(1) == "decode"
+
+
 def test_variant_names():
     for cid in (1, 2, 3, 4, 5):
         wl = workloads.WORKLOADS[cid]

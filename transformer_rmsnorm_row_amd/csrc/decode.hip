@@ -47,7 +47,8 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kStepK = 32;                        // k rows per step
 constexpr int kRing = 3;                          // steps in flight per wave
 constexpr int kCols = 128;                        // one head
-constexpr int kTokens = 64;                       // token capacity (2 blocks of 32)
+constexpr int kTokens = kDecodeTokens;            // token capacity (2 blocks of 32)
+static_assert(kTokens == 64, "two 32-token MFMA blocks per unit");
 constexpr int kWBytes = kStepK * kCols * 2;       // 8 KB weight per step
 constexpr int kXBytes = kTokens * kStepK * 2;     // 4 KB activations per step
 constexpr int kSlot = kWBytes + kXBytes;          // 12 KB

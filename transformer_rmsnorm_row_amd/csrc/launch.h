@@ -63,6 +63,9 @@ hipError_t launch_inv_rms(const void* x, float* inv_rms, int T, int H, float eps
 hipError_t launch_generic(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
 bool prefill_supports(int H, int N, int Nq, int Nkv, int d);
+// Token capacity of one decode launch; larger batches run as consecutive launches of
+// up to this many tokens.
+constexpr int kDecodeTokens = 64;
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
 // gated MLP on the prefill kernel: x, w_norm, w = [H, 2I] (gate | up), q = out [T, I],
 // N = 2I, T, H, eps, bf16

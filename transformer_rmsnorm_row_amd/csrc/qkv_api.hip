@@ -1,6 +1,7 @@
 // C ABI of the fused attention-input library: plan management, argument
 // validation and kernel selection.  Declarations and the contract of every entry
 // point are in include/qkv.h.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -121,9 +122,15 @@ qkv_status ensure_backward_scratch(Plan* pl) {
   return QKV_OK;
 }
 
+// Up to this many tokens the decode kernel, run over consecutive chunks of
+// kDecodeTokens, is faster than the prefill kernel, whose few 256 x 256 tiles then
+// leave most compute units idle while each walks the whole hidden dimension.
+constexpr int64_t kDecodeMaxTokens = 4 * qkv::kDecodeTokens;
+
 int choose_variant(const Plan* pl, int64_t T) {
-  if (pl->bf16 && pl->decode_ok &&
-      qkv::decode_supports((int)T, pl->desc.hidden, pl->N, pl->Nq, pl->Nkv, pl->desc.head_dim))
+  if (pl->bf16 && pl->decode_ok && T <= kDecodeMaxTokens &&
+      qkv::decode_supports((int)std::min<int64_t>(T, qkv::kDecodeTokens), pl->desc.hidden, pl->N, pl->Nq, pl->Nkv,
+                           pl->desc.head_dim))
     return QKV_VARIANT_DECODE;
   if (pl->bf16 && pl->prefill_ok) return QKV_VARIANT_PREFILL;
   return QKV_VARIANT_GENERIC;
@@ -172,9 +179,28 @@ qkv_status launch_forward(Plan* pl, int64_t num_tokens, const void* x, const voi
     case QKV_VARIANT_PREFILL:
       e = qkv::launch_prefill(a, s);
       break;
-    case QKV_VARIANT_DECODE:
-      e = qkv::launch_decode(a, s);
+    case QKV_VARIANT_DECODE: {
+      // one launch per chunk of up to kDecodeTokens tokens, in order on the stream:
+      // the launches share the plan's partial sums and arrival counters
+      const int64_t elem = 2;  // bf16
+      e = hipSuccess;
+      for (int64_t t0 = 0; t0 < num_tokens && e == hipSuccess; t0 += qkv::kDecodeTokens) {
+        qkv::ForwardArgs c = a;
+        c.T = (int)std::min<int64_t>(qkv::kDecodeTokens, num_tokens - t0);
+        c.x = static_cast<const char*>(x) + t0 * a.H * elem;
+        c.pos = pos + t0;
+        c.q = static_cast<char*>(q) + t0 * a.Nq * elem;
+        if (slots) {
+          c.slots = slots + t0;  // k and v are the caches, addressed by slot
+        } else {
+          c.k = static_cast<char*>(k) + t0 * a.Nkv * elem;
+          c.v = static_cast<char*>(v) + t0 * a.Nkv * elem;
+          c.cache_rows = c.T;
+        }
+        e = qkv::launch_decode(c, s);
+      }
       break;
+    }
     default:
       e = qkv::launch_generic(a, s);
       break;
