@@ -70,8 +70,11 @@ typedef enum qkv_dtype {
 typedef enum qkv_variant {
   QKV_VARIANT_GENERIC = 0,  /* fp32 FMA tiles: any supported shape, both dtypes        */
   QKV_VARIANT_PREFILL = 1,  /* bf16 MFMA GEMM, norm-on-load, rotary epilogue           */
-  QKV_VARIANT_DECODE = 2    /* bf16 MFMA weight-streaming kernel for small token counts:
+  QKV_VARIANT_DECODE = 2,   /* bf16 MFMA weight-streaming kernel for small token counts:
                                up to 256 tokens, one launch per 64-token chunk          */
+  QKV_VARIANT_PREFILL_SPLIT = 3  /* the prefill kernel with the hidden dimension split over
+                               two workgroups per tile, when the tiles alone would leave
+                               at least half of the CUs idle                            */
 } qkv_variant;
 
 typedef struct qkv_plan_s* qkv_plan;
@@ -205,7 +208,10 @@ qkv_status qkv_swiglu_forward(int64_t num_tokens, int32_t hidden, int32_t interm
 /* Which variant a forward of num_tokens tokens runs on, in *variant (a qkv_variant):
  * bf16 plans of a shape the decode kernel supports take it up to 256 tokens (as
  * consecutive launches of up to 64 tokens, queued in order on the forward's stream),
- * other bf16 plans of a supported shape the prefill kernel, everything else generic.
+ * other bf16 plans of a supported shape the prefill kernel -- in its split form
+ * (QKV_VARIANT_PREFILL_SPLIT) when T's 256 x 256 tiles number at most 128 and the
+ * hidden size divides into two slices of a multiple of 4 steps of 32, at least 8 --
+ * everything else generic.
  * Host-only; returns QKV_ERR_INVALID_ARG for a bad plan or num_tokens out of range. */
 qkv_status qkv_plan_variant(qkv_plan plan, int64_t num_tokens, int32_t* variant);
 
@@ -217,7 +223,8 @@ qkv_status qkv_plan_destroy(qkv_plan plan);
 /* Static, NUL-terminated description of a status code ("unknown status" otherwise). */
 const char* qkv_status_string(qkv_status status);
 
-/* Static name of a variant ("generic", "prefill", "decode"; "unknown" otherwise). */
+/* Static name of a variant ("generic", "prefill", "decode", "prefill_split"; "unknown"
+ * otherwise). */
 const char* qkv_variant_name(int32_t variant);
 
 #ifdef __cplusplus

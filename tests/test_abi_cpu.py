@@ -37,7 +37,7 @@ def test_status_and_variant_strings():
     assert lib.qkv_status_string(1) == b"invalid argument"
     assert lib.qkv_status_string(2).startswith(b"unsupported")
     assert lib.qkv_status_string(99) == b"unknown status"
-    assert [lib.qkv_variant_name(i) for i in range(3)] == [b"generic", b"prefill", b"decode"]
+    assert [lib.qkv_variant_name(i) for i in range(4)] == [b"generic", b"prefill", b"decode", b"prefill_split"]
     assert lib.qkv_variant_name(7) == b"unknown"
 
 

@@ -64,6 +64,7 @@ CASES = {
                                                   head_dim=256), 650),
     "prefill_d64": (workloads.WORKLOADS[3], dict(batch=1, seq=300, hidden=384, num_q_heads=8, num_kv_heads=2,
                                                  head_dim=64), 650),
+    "prefill_split": (workloads.WORKLOADS[3], dict(batch=1, seq=300), 700),
 }
 
 
@@ -78,7 +79,7 @@ def test_cache_parity(variant):
     v0 = _cache(R, wl.n_kv, wl.torch_dtype, 12)
     kc, vc = k0.to(DEV), v0.to(DEV)
     with qkv.Plan.for_workload(wl) as plan:
-        assert plan.variant(T) == variant.split("_")[0]
+        assert plan.variant(T) == ("prefill_split" if variant == "prefill_split" else variant.split("_")[0])
         q = plan.forward_kv_cache(*_dev(inp), torch.from_numpy(slots).to(DEV), kc, vc)
         torch.cuda.synchronize()
     rq, rk, rv = P.oracle_forward(wl, inp)

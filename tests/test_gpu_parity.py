@@ -95,6 +95,35 @@ def test_prefill_largest_plan():
     print(P.assert_parity(got_rows, ref, P.TOL["bf16"], "largest plan"))
 
 
+SPLIT_CASES = [
+    # (workload, T, overrides): at most 128 tiles of 256 x 256, so K is split over two
+    # workgroups per tile whose partial tiles the last to arrive adds
+    (3, 257, {}),                  # GQA: 2 x 24 = 48 tiles; one real row in the last tile row
+    (3, 777, {}),                  # 4 x 24 = 96 tiles
+    (3, 1280, {}),                 # 5 x 24 = 120 tiles
+    (5, 300, {}),                  # MHA with bias: 2 x 48 = 96 tiles
+    (2, 500, {"hidden": 2048}),    # 96 tiles, 64 steps in 2 slices of 32
+    (3, 300, {"hidden": 2048, "num_q_heads": 8, "num_kv_heads": 2, "head_dim": 64}),  # d = 64: 6 tiles
+    (3, 300, {"hidden": 2048, "num_q_heads": 4, "num_kv_heads": 1, "head_dim": 256}),  # d = 256
+]
+
+
+@pytest.mark.parametrize("cid,T,over", SPLIT_CASES)
+def test_prefill_split_k(cid, T, over):
+    """The split-K form of the prefill kernel: full comparison with the oracle, and two
+    forwards bit for bit equal (the partial tiles are added in slice order, whichever
+    workgroup arrives last)."""
+    wl = shaped(workloads.WORKLOADS[cid].with_tokens(1, T), **over)
+    inp = workloads.make_inputs(wl, seed=11 * T + cid)
+    with qkv.Plan.for_workload(wl) as plan:
+        assert plan.variant(T) == "prefill_split"
+        got = run(plan, inp)
+        again = run(plan, inp)
+    for name, a, b in zip("QKV", got, again):
+        assert torch.equal(a, b), f"{name} differs between two forwards"
+    print(P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], f"{wl.name} split T={T}"))
+
+
 # ---------------------------------------------------------------- ragged sizes, full comparison
 
 MEDIUM = [
@@ -159,7 +188,10 @@ def test_prefill_hidden_sizes(hidden):
                             "per_seq")
     inp = workloads.make_inputs(wl, seed=hidden)
     with qkv.Plan.for_workload(wl) as plan:
-        assert plan.variant(wl.tokens) == "prefill"
+        # 8 tiles: H = 5120 and 8192 split K over two workgroups per tile, the others cannot
+        # (H / 32 steps must split into two multiples of 4)
+        expect = "prefill_split" if hidden in (5120, 8192) else "prefill"
+        assert plan.variant(wl.tokens) == expect
         got = run(plan, inp)
     P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], wl.name)
 
@@ -319,11 +351,14 @@ def test_decode_in_chunks(T):
 
 
 def test_decode_chunk_boundary():
-    """The decode kernel serves up to 256 tokens of a plan; 257 go to the prefill kernel."""
-    wl = workloads.WORKLOADS[4].with_tokens(257, 1)
+    """The decode kernel serves up to 256 tokens of a plan; 257 go to the prefill kernel
+    (in its split-K form while the tiles number at most 128: 24 per 256 tokens here)."""
+    wl = workloads.WORKLOADS[4].with_tokens(1537, 1)
     with qkv.Plan.for_workload(wl) as plan:
         assert plan.variant(256) == "decode"
-        assert plan.variant(257) == "prefill"
+        assert plan.variant(257) == "prefill_split"
+        assert plan.variant(1280) == "prefill_split"   # 5 x 24 = 120 tiles
+        assert plan.variant(1281) == "prefill"         # 6 x 24 = 144 tiles
         assert plan.variant(1) == "decode"
 
 

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libqkv_mi355x.so")
 
 QKV_OK, QKV_ERR_INVALID_ARG, QKV_ERR_UNSUPPORTED, QKV_ERR_HIP, QKV_ERR_OUT_OF_MEMORY = range(5)
 QKV_F32, QKV_BF16 = 0, 1
-VARIANTS = {0: "generic", 1: "prefill", 2: "decode"}
+VARIANTS = {0: "generic", 1: "prefill", 2: "decode", 3: "prefill_split"}
 
 # Entry points of include/qkv.h: name -> (restype, argtypes)
 _vp = ctypes.c_void_p

@@ -20,6 +20,12 @@ struct ForwardArgs {
   const double* rev_freq;  // [head_dim/2] rotary frequencies, revolutions per position
   float* partials;         // decode scratch
   uint32_t* counters;      // decode scratch
+  // prefill with the hidden dimension split over several workgroups per tile (when the
+  // tiles alone would leave most CUs idle): fp32 partial tiles and per-tile arrival
+  // counters, or null when the plan has none
+  float* kpart;
+  uint32_t* kcount;
+  int kpart_units;         // partial tiles kpart holds
   // KV-cache form: when non-null, K and V of token t go to row slots[t] of k and v,
   // which then hold cache_rows rows; tokens whose slot is outside [0, cache_rows)
   // write no K/V.  Q stays dense.
@@ -63,6 +69,17 @@ hipError_t launch_inv_rms(const void* x, float* inv_rms, int T, int H, float eps
 hipError_t launch_generic(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
 bool prefill_supports(int H, int N, int Nq, int Nkv, int d);
+// The split-K form of the prefill kernel (two K slices per 256 x 256 tile, partial
+// tiles added by the last-arriving workgroup) is used up to this many tiles, one arrival
+// counter each.
+constexpr int kPrefillSplitMaxTiles = 128;
+// Partial tiles a plan of max_tokens tokens and N columns needs for the split-K form of
+// the prefill kernel, and their fp32 element count.
+int prefill_split_units(int max_tokens, int N);
+// K slices per tile the prefill kernel uses for T tokens (1: the plain form), given a
+// plan whose split scratch holds `units` partial tiles.
+int prefill_split_count(int T, int H, int N, int units);
+size_t prefill_split_floats(int units);
 // Token capacity of one decode launch; larger batches run as consecutive launches of
 // up to this many tokens.
 constexpr int kDecodeTokens = 64;

@@ -121,16 +121,30 @@ __device__ __forceinline__ int pair_block(int slot) {
   return kD == 128 ? 128 * (slot >> 1) + 32 * (slot & 1) : (kD == 256 ? 32 * slot : 64 * slot);
 }
 
-template <int kEpi, int kD>
-__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
+// Floats of one partial tile of the split-K form: the 256 x 256 fp32 sums, then the
+// 256 rows' partial sums of squares.
+constexpr int kPartFloats = BM * BN + BM;
 
-  // ---- tile selection: XCD-contiguous numbering, then groups of kGroupM row panels
+template <int kEpi, int kD, int kSplit>
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int tiles_m, int tiles_n) {
+  constexpr bool kSplitK = kSplit > 1;
+  constexpr int nsplit = kSplit;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
+  __shared__ int s_last;
+
+  // ---- tile selection: XCD-contiguous numbering, then groups of kGroupM row panels.
+  // Split-K form: workgroup b takes K slice b % nsplit of tile b / nsplit.
   const int G = tiles_m * tiles_n;
   const int bid = blockIdx.x;
-  const int xcd = bid & 7, local = bid >> 3;
-  const int q8 = G >> 3, r8 = G & 7;
-  const int L = (xcd < r8) ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
+  int L, ks = 0;
+  if constexpr (kSplitK) {
+    L = bid / nsplit;
+    ks = bid % nsplit;
+  } else {
+    const int xcd = bid & 7, local = bid >> 3;
+    const int q8 = G >> 3, r8 = G & 7;
+    L = (xcd < r8) ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
+  }
   const int group = L / (kGroupM * tiles_n);
   const int first_m = group * kGroupM;
   const int gm = min(tiles_m - first_m, kGroupM);
@@ -147,13 +161,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   const int blk = pair_block<kD>(slot);  // tile column of the wave's first block
   const int c0 = blk % kD;             // first rotation-pair index of this wave
   const int H = a.H, N = a.N, T = a.T;
+  // 32-row steps of this workgroup's K range: all of H, or slice ks of nsplit
+  const int nk = kSplitK ? H / BK / nsplit : H / BK;  // multiple of 4, at least 4
+  const uint32_t kofs = kSplitK ? (uint32_t)(ks * nk * BK) : 0u;  // first k of the range
   const uint32_t fl = lane & 31, fh = lane >> 5;
 
   // ---- activation staging: thread u of its group owns chunk kc of the group's rows
   // ar and ar + 64 (tile rows 128 grp + ar + 64 j)
   const uint32_t u = tid & 255, kc = u & 3, ar = u >> 2;
   const uint32_t arow = 128u * grp + ar;
-  const uint32_t x_voff = ((uint32_t)(m0 + arow) * H + kc * 8u) * 2u;
+  const uint32_t x_voff = ((uint32_t)(m0 + arow) * H + kofs + kc * 8u) * 2u;
   const uint32_t x_jstep = 64u * H * 2u;
   const uint32_t a_woff = kABase + a_off(arow, kc);  // row + 64 keeps the swizzle: + 4096
 
@@ -173,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
       const uint32_t f = 128u * (uint32_t)tn + 64u * h + (wi & 63u);
       col = wi < 64u ? f : (uint32_t)(N / 2) + f;
     }
-    b_voff[i] = ((4u * wave + krow) * N + col) * 2u;
+    b_voff[i] = ((kofs + 4u * wave + krow) * N + col) * 2u;
   }
   const uint64_t wbase = reinterpret_cast<uint64_t>(a.w);
   const u32x4 w_rsrc = {(uint32_t)wbase, (uint32_t)(wbase >> 32), (uint32_t)H * (uint32_t)N * 2u,
@@ -232,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     const uint32_t k0 = (uint32_t)t * BK;
     gx[set][0] = asm_load16(x_voff + k0 * 2u, x_rsrc);
     gx[set][1] = asm_load16(x_voff + x_jstep + k0 * 2u, x_rsrc);
-    gw[set] = asm_load16((k0 + kc * 8u) * 2u, n_rsrc);
+    gw[set] = asm_load16((kofs + k0 + kc * 8u) * 2u, n_rsrc);
   };
   constexpr int kWOps = 2, kXOps = 3;
   // the registers of a set become usable only after an explicit wait
@@ -355,7 +372,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     barrier();
   };
 
-  const int nk = H / BK;  // multiple of 4, at least 4
   // The epilogue's per-row and per-column inputs, requested now so that their latency
   // hides under the main loop: position (and cache slot) of row tid, bias of this
   // lane's two columns, rotation frequency of its pair.
@@ -438,7 +454,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
       float v = ss[j];
       v += __shfl_xor(v, 1, 64);
       v += __shfl_xor(v, 2, 64);
-      if (kc == 0) s_rinv[arow + 64u * j] = rsqrtf(v / (float)H + a.eps);
+      // the split-K form keeps the raw partial sum until the slices are added
+      if (kc == 0) s_rinv[arow + 64u * j] = kSplitK ? v : rsqrtf(v / (float)H + a.eps);
     }
     if (tid < BM) {
       s_pos[tid] = pos_pref;
@@ -446,6 +463,93 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     }
   }
   __syncthreads();
+
+  if constexpr (kSplitK) {
+    // ---- split-K: this workgroup's partial tile goes to plan scratch and is counted
+    // in per tile; the workgroup that arrives last adds the nsplit partial tiles in
+    // slice order (so the result does not depend on the arrival order), then runs the
+    // epilogue.  Partial tile layout: 16-byte chunk j (0..31) of thread tid at
+    // j * 512 + tid, chunk j holding registers 4 (j % 4) .. + 3 of accumulator j / 4;
+    // then the 256 row sums of squares.  Stores and loads are device-coherent (sc1),
+    // since the slices of a tile run on different XCDs.
+    const uint64_t pbase = reinterpret_cast<uint64_t>(a.kpart);
+    const u32x4 p_rsrc = {(uint32_t)pbase, (uint32_t)(pbase >> 32), (uint32_t)a.kpart_units * kPartFloats * 4u,
+                          (uint32_t)kBufferWord3};
+    // byte offsets: a wave-uniform part (partial tile, chunk) in the scalar offset
+    // operand, the thread's 16 or 4 bytes in the vector one
+    const uint32_t own = (uint32_t)__builtin_amdgcn_readfirstlane((L * nsplit + ks) * kPartFloats * 4);
+    const uint32_t t16 = (uint32_t)tid * 16u, t4 = (uint32_t)tid * 4u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int ai = j >> 2, q4 = j & 3;
+      const f32x16& ac = acc[ai >> 1][ai & 1];
+      const f32x4 v = {ac[4 * q4], ac[4 * q4 + 1], ac[4 * q4 + 2], ac[4 * q4 + 3]};
+      asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen sc1" ::"v"(__builtin_bit_cast(u32x4, v)), "v"(t16),
+                   "s"(p_rsrc), "s"(own + (uint32_t)(j * kThreads * 16))
+                   : "memory");
+    }
+    if (tid < BM)
+      asm volatile("buffer_store_dword %0, %1, %2, %3 offen sc1" ::"v"(s_rinv[tid]), "v"(t4), "s"(p_rsrc),
+                   "s"(own + (uint32_t)(BM * BN * 4))
+                   : "memory");
+    // every store of the workgroup complete before it is counted in
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&a.kcount[L], 1u) == (unsigned)(nsplit - 1);
+    __syncthreads();
+    if (!s_last) return;
+    // The nsplit partial tiles in slice order, 8 chunks (32 KB per workgroup) per batch,
+    // double-buffered: batch b holds chunks 8 (b % 4) .. + 7 of slice b / 4, and the
+    // next batch is in flight while one is added in.
+    constexpr int kBatches = 4 * kSplit;
+    u32x4 buf[2][8];
+#pragma unroll
+    for (int b = 0; b <= kBatches; ++b) {
+      if (b < kBatches) {
+        const uint32_t uo = (uint32_t)__builtin_amdgcn_readfirstlane((L * nsplit + b / 4) * kPartFloats * 4);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen sc1"
+                       : "=v"(buf[b & 1][jj])
+                       : "v"(t16), "s"(p_rsrc), "s"(uo + (uint32_t)((8 * (b & 3) + jj) * kThreads * 16))
+                       : "memory");
+      }
+      if (b == 0) continue;
+      // batch b - 1 has landed once at most the 8 loads of batch b are outstanding
+      if (b < kBatches)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const int pb = b - 1, sp = pb / 4;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        asm volatile("" : "+v"(buf[pb & 1][jj]));
+        const int j = 8 * (pb & 3) + jj, ai = j >> 2, q4 = j & 3;
+        f32x16& ac = acc[ai >> 1][ai & 1];
+        const f32x4 f = __builtin_bit_cast(f32x4, buf[pb & 1][jj]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ac[4 * q4 + e] = sp == 0 ? f[e] : ac[4 * q4 + e] + f[e];
+      }
+      // the batch's adds happen here, not later: its registers are free for the next
+      asm volatile("" : "+v"(acc[pb & 3][0]), "+v"(acc[pb & 3][1]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (tid < BM) {
+      float tot = 0.f;
+      for (int sp = 0; sp < nsplit; ++sp) {
+        uint32_t u;
+        asm volatile("buffer_load_dword %0, %1, %2, %3 offen sc1\n\ts_waitcnt vmcnt(0)"
+                     : "=v"(u)
+                     : "v"(t4), "s"(p_rsrc),
+                       "s"((uint32_t)__builtin_amdgcn_readfirstlane(((L * nsplit + sp) * kPartFloats + BM * BN) * 4))
+                     : "memory");
+        tot = sp == 0 ? __uint_as_float(u) : tot + __uint_as_float(u);
+      }
+      s_rinv[tid] = rsqrtf(tot / (float)H + a.eps);
+    }
+    __syncthreads();
+    if (tid == 0) a.kcount[L] = 0u;  // ready for the next forward through the plan
+  }
 
   if constexpr (kEpi == kEpiSwiglu) {
     // ---- epilogue: out = SiLU(g) * u with g, u the gate and up sums scaled by 1/rms;
@@ -563,24 +667,52 @@ bool prefill_supports(int H, int N, int Nq, int Nkv, int d) {
          Nkv % 128 == 0 && Nq % d == 0 && Nkv % d == 0;
 }
 
-hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream) {
-  const int tiles_m = (a.T + BM - 1) / BM, tiles_n = a.N / BN;
-  const dim3 grid(tiles_m * tiles_n), block(kThreads);
-  if (a.d == 64)
-    prefill_kernel<kEpiQkv, 64><<<grid, block, 0, stream>>>(a, tiles_m, tiles_n);
-  else if (a.d == 256)
-    prefill_kernel<kEpiQkv, 256><<<grid, block, 0, stream>>>(a, tiles_m, tiles_n);
+// K slices per tile: 2 (the split-K form) when the tiles alone would leave at least half
+// of the 256 CUs idle, else 1 (the plain form).  Each slice keeps at least 8 steps of 32
+// rows and a multiple of 4 of them.  Four slices were measured too: each workgroup's
+// loop is shorter, but the last-arriving one then reads four partial tiles, and the
+// forward was 1-5% slower than with two.
+int prefill_splits(const ForwardArgs& a, int tiles) {
+  if (!a.kpart || !a.kcount) return 1;
+  return prefill_split_count(a.T, a.H, a.N, a.kpart_units);
+}
+
+template <int kD>
+hipError_t launch_prefill_d(const ForwardArgs& a, int tiles_m, int tiles_n, hipStream_t stream) {
+  const int tiles = tiles_m * tiles_n, s = prefill_splits(a, tiles);
+  if (s == 2)
+    prefill_kernel<kEpiQkv, kD, 2><<<dim3(tiles * 2), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
   else
-    prefill_kernel<kEpiQkv, 128><<<grid, block, 0, stream>>>(a, tiles_m, tiles_n);
+    prefill_kernel<kEpiQkv, kD, 1><<<dim3(tiles), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
   return hipGetLastError();
 }
+
+hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream) {
+  const int tiles_m = (a.T + BM - 1) / BM, tiles_n = a.N / BN;
+  if (a.d == 64) return launch_prefill_d<64>(a, tiles_m, tiles_n, stream);
+  if (a.d == 256) return launch_prefill_d<256>(a, tiles_m, tiles_n, stream);
+  return launch_prefill_d<128>(a, tiles_m, tiles_n, stream);
+}
+
+int prefill_split_count(int T, int H, int N, int units) {
+  const int tiles = (T + BM - 1) / BM * (N / BN), nk = H / BK;
+  if (tiles > kPrefillSplitMaxTiles) return 1;
+  return tiles * 2 <= units && nk % 8 == 0 && nk / 2 >= 8 ? 2 : 1;
+}
+
+int prefill_split_units(int max_tokens, int N) {
+  const int tiles = (max_tokens + BM - 1) / BM * (N / BN);
+  return 2 * (tiles < kPrefillSplitMaxTiles ? tiles : kPrefillSplitMaxTiles);
+}
+
+size_t prefill_split_floats(int units) { return (size_t)units * kPartFloats; }
 
 bool swiglu_supports(int H, int I) { return H % (4 * BK) == 0 && I % 128 == 0; }
 
 hipError_t launch_swiglu(const ForwardArgs& a, hipStream_t stream) {
   // a.N = 2I columns of [gate | up]; the output (a.q) is [T, I]
   const int tiles_m = (a.T + BM - 1) / BM, tiles_n = a.N / BN;
-  prefill_kernel<kEpiSwiglu, 128><<<dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
+  prefill_kernel<kEpiSwiglu, 128, 1><<<dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -30,6 +30,9 @@ struct Plan {
   double* rev_freq;   // [head_dim/2]
   float* partials;    // decode partial sums
   uint32_t* counters; // decode arrival counters
+  float* kpart;       // split-K prefill: partial tiles
+  uint32_t* kcount;   // split-K prefill: per-tile arrival counters
+  int kpart_units;    // partial tiles kpart holds
   // backward scratch, allocated by the first qkv_backward through the plan
   void* bwd_gy;         // [max_tokens, N] plan dtype
   void* bwd_act;        // [max_tokens, H] plan dtype
@@ -88,6 +91,8 @@ void free_scratch(Plan* pl) {
   if (pl->rev_freq) (void)hipFree(pl->rev_freq);
   if (pl->partials) (void)hipFree(pl->partials);
   if (pl->counters) (void)hipFree(pl->counters);
+  if (pl->kpart) (void)hipFree(pl->kpart);
+  if (pl->kcount) (void)hipFree(pl->kcount);
   if (pl->bwd_gy) (void)hipFree(pl->bwd_gy);
   if (pl->bwd_act) (void)hipFree(pl->bwd_act);
   if (pl->bwd_ga) (void)hipFree(pl->bwd_ga);
@@ -97,6 +102,8 @@ void free_scratch(Plan* pl) {
   pl->rev_freq = nullptr;
   pl->partials = nullptr;
   pl->counters = nullptr;
+  pl->kpart = nullptr;
+  pl->kcount = nullptr;
   pl->bwd_gy = pl->bwd_act = nullptr;
   pl->bwd_ga = pl->bwd_partial = nullptr;
   pl->blas = nullptr;
@@ -132,7 +139,10 @@ int choose_variant(const Plan* pl, int64_t T) {
       qkv::decode_supports((int)std::min<int64_t>(T, qkv::kDecodeTokens), pl->desc.hidden, pl->N, pl->Nq, pl->Nkv,
                            pl->desc.head_dim))
     return QKV_VARIANT_DECODE;
-  if (pl->bf16 && pl->prefill_ok) return QKV_VARIANT_PREFILL;
+  if (pl->bf16 && pl->prefill_ok)
+    return pl->kpart && qkv::prefill_split_count((int)T, pl->desc.hidden, pl->N, pl->kpart_units) > 1
+               ? QKV_VARIANT_PREFILL_SPLIT
+               : QKV_VARIANT_PREFILL;
   return QKV_VARIANT_GENERIC;
 }
 
@@ -162,6 +172,9 @@ qkv_status launch_forward(Plan* pl, int64_t num_tokens, const void* x, const voi
   a.rev_freq = pl->rev_freq;
   a.partials = pl->partials;
   a.counters = pl->counters;
+  a.kpart = pl->kpart;
+  a.kcount = pl->kcount;
+  a.kpart_units = pl->kpart_units;
   a.slots = slots;
   a.cache_rows = slots ? cache_rows : (int)num_tokens;
   a.T = (int)num_tokens;
@@ -177,6 +190,7 @@ qkv_status launch_forward(Plan* pl, int64_t num_tokens, const void* x, const voi
   hipError_t e;
   switch (choose_variant(pl, num_tokens)) {
     case QKV_VARIANT_PREFILL:
+    case QKV_VARIANT_PREFILL_SPLIT:  // the launcher makes the same split choice
       e = qkv::launch_prefill(a, s);
       break;
     case QKV_VARIANT_DECODE: {
@@ -244,6 +258,16 @@ qkv_status qkv_plan_create(const qkv_plan_desc* desc, qkv_plan* out_plan) {
     ok = hipMalloc(&pl->partials, sizeof(float) * qkv::decode_scratch_floats(desc->hidden, pl->N)) == hipSuccess &&
          hipMalloc(&pl->counters, sizeof(uint32_t) * nheads) == hipSuccess &&
          hipMemset(pl->counters, 0, sizeof(uint32_t) * nheads) == hipSuccess &&
+         hipDeviceSynchronize() == hipSuccess;
+  }
+  if (ok && pl->prefill_ok) {
+    // partial tiles of the split-K prefill form (used when the tiles alone would leave
+    // most CUs idle) and one arrival counter per tile (zeroed once; the kernel leaves
+    // them at zero after every forward)
+    pl->kpart_units = qkv::prefill_split_units((int)desc->max_tokens, pl->N);
+    ok = hipMalloc(&pl->kpart, sizeof(float) * qkv::prefill_split_floats(pl->kpart_units)) == hipSuccess &&
+         hipMalloc(&pl->kcount, sizeof(uint32_t) * qkv::kPrefillSplitMaxTiles) == hipSuccess &&
+         hipMemset(pl->kcount, 0, sizeof(uint32_t) * qkv::kPrefillSplitMaxTiles) == hipSuccess &&
          hipDeviceSynchronize() == hipSuccess;
   }
   if (!ok) {
@@ -443,6 +467,7 @@ const char* qkv_variant_name(int32_t variant) {
     case QKV_VARIANT_GENERIC: return "generic";
     case QKV_VARIANT_PREFILL: return "prefill";
     case QKV_VARIANT_DECODE: return "decode";
+    case QKV_VARIANT_PREFILL_SPLIT: return "prefill_split";
   }
   return "unknown";
 }
