@@ -387,6 +387,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama7b_prefill")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload's shape at this many tokens (one sequence) instead of its own")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-extra", action="store_true",
@@ -420,6 +422,8 @@ def main() -> int:
     import workloads
 
     wl = workloads.BY_NAME[args.workload]
+    if args.tokens:
+        wl = wl.with_tokens(1, args.tokens)
     inp = workloads.make_inputs(wl)
     bufs = device_inputs(wl, inp)
     plan = qkv.Plan.for_workload(wl)
