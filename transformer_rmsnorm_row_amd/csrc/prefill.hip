@@ -466,9 +466,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
 
   if constexpr (kSplitK) {
     // ---- split-K: this workgroup's partial tile goes to plan scratch and is counted
-    // in per tile; the workgroup that arrives last adds the nsplit partial tiles in
-    // slice order (so the result does not depend on the arrival order), then runs the
-    // epilogue.  Partial tile layout: 16-byte chunk j (0..31) of thread tid at
+    // in per tile; the workgroup that arrives last adds the other slice's partial tile to
+    // its own, then runs the epilogue.  Partial tile layout: 16-byte chunk j (0..31) of thread tid at
     // j * 512 + tid, chunk j holding registers 4 (j % 4) .. + 3 of accumulator j / 4;
     // then the 256 row sums of squares.  Stores and loads are device-coherent (sc1),
     // since the slices of a tile run on different XCDs.
@@ -498,54 +497,50 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     if (tid == 0) s_last = atomicAdd(&a.kcount[L], 1u) == (unsigned)(nsplit - 1);
     __syncthreads();
     if (!s_last) return;
-    // The nsplit partial tiles in slice order, 8 chunks (32 KB per workgroup) per batch,
-    // double-buffered: batch b holds chunks 8 (b % 4) .. + 7 of slice b / 4, and the
-    // next batch is in flight while one is added in.
-    constexpr int kBatches = 4 * kSplit;
+    // Two slices: the sum is own + other, and floating-point addition is commutative, so
+    // the result does not depend on which workgroup arrives last.  The other slice's
+    // partial tile is read in 8-chunk batches (32 KB per workgroup), double-buffered:
+    // the next batch is in flight while one is added in.
+    static_assert(kSplit == 2, "the reduction below adds exactly two partial tiles");
+    const uint32_t other = (uint32_t)__builtin_amdgcn_readfirstlane((L * nsplit + (1 - ks)) * kPartFloats * 4);
     u32x4 buf[2][8];
 #pragma unroll
-    for (int b = 0; b <= kBatches; ++b) {
-      if (b < kBatches) {
-        const uint32_t uo = (uint32_t)__builtin_amdgcn_readfirstlane((L * nsplit + b / 4) * kPartFloats * 4);
+    for (int b = 0; b <= 4; ++b) {
+      if (b < 4) {
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
           asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen sc1"
                        : "=v"(buf[b & 1][jj])
-                       : "v"(t16), "s"(p_rsrc), "s"(uo + (uint32_t)((8 * (b & 3) + jj) * kThreads * 16))
+                       : "v"(t16), "s"(p_rsrc), "s"(other + (uint32_t)((8 * b + jj) * kThreads * 16))
                        : "memory");
       }
       if (b == 0) continue;
       // batch b - 1 has landed once at most the 8 loads of batch b are outstanding
-      if (b < kBatches)
+      if (b < 4)
         asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
       else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      const int pb = b - 1, sp = pb / 4;
+      const int pb = b - 1;
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         asm volatile("" : "+v"(buf[pb & 1][jj]));
-        const int j = 8 * (pb & 3) + jj, ai = j >> 2, q4 = j & 3;
+        const int j = 8 * pb + jj, ai = j >> 2, q4 = j & 3;
         f32x16& ac = acc[ai >> 1][ai & 1];
         const f32x4 f = __builtin_bit_cast(f32x4, buf[pb & 1][jj]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ac[4 * q4 + e] = sp == 0 ? f[e] : ac[4 * q4 + e] + f[e];
+        for (int e = 0; e < 4; ++e) ac[4 * q4 + e] += f[e];
       }
       // the batch's adds happen here, not later: its registers are free for the next
-      asm volatile("" : "+v"(acc[pb & 3][0]), "+v"(acc[pb & 3][1]));
+      asm volatile("" : "+v"(acc[pb][0]), "+v"(acc[pb][1]));
       __builtin_amdgcn_sched_barrier(0);
     }
     if (tid < BM) {
-      float tot = 0.f;
-      for (int sp = 0; sp < nsplit; ++sp) {
-        uint32_t u;
-        asm volatile("buffer_load_dword %0, %1, %2, %3 offen sc1\n\ts_waitcnt vmcnt(0)"
-                     : "=v"(u)
-                     : "v"(t4), "s"(p_rsrc),
-                       "s"((uint32_t)__builtin_amdgcn_readfirstlane(((L * nsplit + sp) * kPartFloats + BM * BN) * 4))
-                     : "memory");
-        tot = sp == 0 ? __uint_as_float(u) : tot + __uint_as_float(u);
-      }
-      s_rinv[tid] = rsqrtf(tot / (float)H + a.eps);
+      uint32_t u;
+      asm volatile("buffer_load_dword %0, %1, %2, %3 offen sc1\n\ts_waitcnt vmcnt(0)"
+                   : "=v"(u)
+                   : "v"(t4), "s"(p_rsrc), "s"(other + (uint32_t)(BM * BN * 4))
+                   : "memory");
+      s_rinv[tid] = rsqrtf((s_rinv[tid] + __uint_as_float(u)) / (float)H + a.eps);
     }
     __syncthreads();
     if (tid == 0) a.kcount[L] = 0u;  // ready for the next forward through the plan
