@@ -117,7 +117,7 @@ def time_forward_kv_cache(qkv, wl, plan, bufs, steps: int, warmup: int, cap: int
     return start.elapsed_time(end) / 1e3 / steps
 
 
-def time_forward_cold(plan, bufs, calls: int = 20, flush_mib: int = 512):
+def time_forward_cold(plan, bufs, calls: int = 50, flush_mib: int = 512):
     """Per-call times with the last-level cache flushed before each call: a 512 MiB
     buffer is rewritten between calls so x and W come from HBM.  Returns seconds."""
     import torch
