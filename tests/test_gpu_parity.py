@@ -198,9 +198,18 @@ def test_prefill_hidden_sizes(hidden):
 
 # ---------------------------------------------------------------- inputs the workloads cannot see
 
-def _pin_case(kind, dtype="bf16"):
-    wl = workloads.Workload(8, f"pin_{kind}", 1, 96, 512, 4, 2, 128, kind == "big_bias", 1e4, 1e-6, dtype,
-                            "per_seq")
+# shapes the special inputs run on, one per bf16 kernel: (tokens, hidden, variant)
+PIN_SHAPES = {
+    "decode": (96, 512, "decode"),            # two 64-token chunks
+    "prefill": (300, 384, "prefill"),         # 12 K steps: no split
+    "split": (300, 512, "prefill_split"),     # 8 tiles, 16 K steps in two slices
+}
+
+
+def _pin_case(kind, dtype="bf16", shape="decode"):
+    T, H, _ = PIN_SHAPES[shape]
+    bias = kind in ("big_bias", "zero_rows")
+    wl = workloads.Workload(8, f"pin_{kind}_{shape}", 1, T, H, 4, 2, 128, bias, 1e4, 1e-6, dtype, "per_seq")
     inp = workloads.make_inputs(wl, seed=404)
     g = torch.Generator().manual_seed(405)
     dt = wl.torch_dtype
@@ -209,25 +218,41 @@ def _pin_case(kind, dtype="bf16"):
         inp["x"] = (inp["x"].float() * scale).to(dt)
     elif kind == "small_rows":
         inp["x"] = (inp["x"].float() * 1e-3).to(dt)
+    elif kind == "huge_rows":
+        inp["x"] = (inp["x"].float() * 1e4).to(dt)
+    elif kind == "zero_rows":
+        # all-zero rows: 1/rms = 1/sqrt(eps), the normalised row is zero, and Q/K/V are the
+        # bias (Q and K rotated); the first and last rows of every tile and chunk among them
+        x = inp["x"].float()
+        for t in {0, 1, 63, 64, 95, wl.tokens - 1, 255 % wl.tokens, 256 % wl.tokens}:
+            x[t] = 0.0
+        inp["x"] = x.to(dt)
     elif kind == "big_bias":
         inp["bias"] = torch.randn(wl.n_total, generator=g).to(dt)
     elif kind == "one_hot":
         W = torch.zeros(wl.hidden, wl.n_total)
-        for j, (k0, n0) in enumerate([(0, 0), (511, wl.n_q - 1), (17, wl.n_q), (300, wl.n_total - 1)]):
+        for j, (k0, n0) in enumerate([(0, 0), (H - 1, wl.n_q - 1), (17, wl.n_q), (300, wl.n_total - 1)]):
             W[k0, n0] = 1.0
         inp["w_qkv"] = W.to(dt)
     elif kind == "positions":
-        inp["pos"] = torch.tensor([0, -1, -32768, 2**31 - 1, -(2**31), 1, 65535, 4096] * 12, dtype=torch.int32)
+        base = torch.tensor([0, -1, -32768, 2**31 - 1, -(2**31), 1, 65535, 4096], dtype=torch.int32)
+        inp["pos"] = base.repeat((wl.tokens + 7) // 8)[: wl.tokens].contiguous()
     return wl, inp
 
 
-@pytest.mark.parametrize("kind", ["row_scaled", "small_rows", "big_bias", "one_hot", "positions"])
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_pinning_inputs(kind, dtype):
-    wl, inp = _pin_case(kind, dtype)
+PIN_KINDS = ["row_scaled", "small_rows", "huge_rows", "zero_rows", "big_bias", "one_hot", "positions"]
+
+
+@pytest.mark.parametrize("kind", PIN_KINDS)
+@pytest.mark.parametrize("dtype,shape", [("bf16", "decode"), ("bf16", "prefill"), ("bf16", "split"),
+                                         ("fp32", "decode")])
+def test_pinning_inputs(kind, dtype, shape):
+    wl, inp = _pin_case(kind, dtype, shape)
     with qkv.Plan.for_workload(wl) as plan:
+        if dtype == "bf16":
+            assert plan.variant(wl.tokens) == PIN_SHAPES[shape][2]
         got = run(plan, inp)
-    P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL[dtype], f"{kind}/{dtype}")
+    P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL[dtype], f"{kind}/{dtype}/{shape}")
 
 
 def test_eps_is_applied():
