@@ -38,8 +38,9 @@
  * Ownership: the caller owns every tensor, allocates the outputs, and keeps all
  * buffers alive until the work queued on `stream` has finished.  A plan owns only
  * its device scratch (per-token inverse RMS values, decode partial sums and
- * counters, the rotary frequency table), allocated on the device that is current
- * when the plan is created and freed by qkv_plan_destroy.
+ * counters, the split-K prefill form's partial tiles -- up to 67 MB -- and counters,
+ * the rotary frequency table), allocated on the device that is current when the plan
+ * is created and freed by qkv_plan_destroy.
  *
  * Errors: every call returns a status code; nothing is thrown across the ABI.
  * Arguments are validated before any HIP call is made.
