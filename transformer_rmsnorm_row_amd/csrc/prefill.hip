@@ -38,6 +38,12 @@
 //     pos * theta^(-2i/d) (turn count reduced in fp64, hardware sin/cos on the
 //     fraction of a turn); bf16 results staged through LDS and stored with 16-byte
 //     writes.
+//   * Split-K form (kSplit = 2), for token counts whose tiles number at most 128 and
+//     would leave most CUs idle: the two halves of a tile's K range run in two
+//     workgroups; each stores its fp32 partial tile and partial row sums of squares to
+//     plan scratch and counts itself in, and the second to arrive adds the other's
+//     partial to its own registers (two terms commute, so the result does not depend
+//     on the arrival order) before the same epilogue.
 #include <type_traits>
 
 #include "device_common.h"
