@@ -206,6 +206,8 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(BackwardArgs b, int
   const int per = (b.T + chunks - 1) / chunks;
   const int t0 = blockIdx.y * per, t1 = min(b.T, t0 + per);
   float s = 0.f;
+  // unrolled so that the loads of several tokens are in flight; the adds keep token order
+#pragma unroll 8
   for (int t = t0; t < t1; ++t) {
     if constexpr (kMode == 0)
       s += ld<BF16>(b.gy, (size_t)t * ncols + c);
@@ -221,6 +223,8 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* partial,
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= ncols) return;
   float s = 0.f;
+  // unrolled so that the chunks' loads are in flight together; the adds keep chunk order
+#pragma unroll 16
   for (int j = 0; j < chunks; ++j) s += partial[(size_t)j * ncols + c];
   st<BF16>(out, c, s);
 }
