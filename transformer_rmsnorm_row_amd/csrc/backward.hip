@@ -142,12 +142,35 @@ __global__ __launch_bounds__(256) void unrotate_kernel(BackwardArgs b) {
 }
 
 // One wave per token: r[t] and the normalised activations a = x r w in the plan dtype.
-template <bool BF16>
+// KIT > 0: H = 512 KIT, and the lane's KIT x 8 values of the row stay in registers
+// between the two passes (same arithmetic, same order); KIT = 0: any H, row read twice.
+template <bool BF16, int KIT>
 __global__ __launch_bounds__(256) void activations_kernel(BackwardArgs b) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= b.T) return;
   const size_t row = (size_t)t * b.H;
+  if constexpr (KIT > 0) {
+    float v[KIT][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int m = 0; m < KIT; ++m) {
+      ld8<BF16>(b.x, row + lane * 8 + 512 * m, v[m]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss = fmaf(v[m][j], v[m][j], ss);
+    }
+    const float r = rsqrtf(wave_sum(ss) / (float)b.H + b.eps);
+    if (lane == 0) b.inv_rms[t] = r;
+#pragma unroll
+    for (int m = 0; m < KIT; ++m) {
+      float w[8];
+      ld8<BF16>(b.w_norm, lane * 8 + 512 * m, w);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[m][j] = v[m][j] * r * w[j];
+      st8<BF16>(b.act, row + lane * 8 + 512 * m, v[m]);
+    }
+    return;
+  }
   float ss = 0.f;
   for (int k = lane * 8; k < b.H; k += 512) {
     float v[8];
@@ -167,13 +190,39 @@ __global__ __launch_bounds__(256) void activations_kernel(BackwardArgs b) {
   }
 }
 
-// One wave per token: dx from ga (fp32), x, w and r.
-template <bool BF16>
+// One wave per token: dx from ga (fp32), x, w and r.  KIT as for the activations:
+// the lane's ga and x values stay in registers between the inner product and dx.
+template <bool BF16, int KIT>
 __global__ __launch_bounds__(256) void norm_grad_kernel(BackwardArgs b) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= b.T) return;
   const size_t row = (size_t)t * b.H;
+  if constexpr (KIT > 0) {
+    float g[KIT][8], x[KIT][8];
+    float inner = 0.f;
+#pragma unroll
+    for (int m = 0; m < KIT; ++m) {
+      float w[8];
+      ld8<false>(b.ga, row + lane * 8 + 512 * m, g[m]);
+      ld8<BF16>(b.w_norm, lane * 8 + 512 * m, w);
+      ld8<BF16>(b.x, row + lane * 8 + 512 * m, x[m]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) inner = fmaf(g[m][j] * w[j], x[m][j], inner);
+    }
+    inner = wave_sum(inner);
+    const float r = b.inv_rms[t];
+    const float c2 = r * r * r / (float)b.H * inner;
+#pragma unroll
+    for (int m = 0; m < KIT; ++m) {
+      float w[8];
+      ld8<BF16>(b.w_norm, lane * 8 + 512 * m, w);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) g[m][j] = r * w[j] * g[m][j] - c2 * x[m][j];
+      st8<BF16>(b.dx, row + lane * 8 + 512 * m, g[m]);
+    }
+    return;
+  }
   float inner = 0.f;
   for (int k = lane * 8; k < b.H; k += 512) {
     float g[8], w[8], x[8];
@@ -248,14 +297,26 @@ hipError_t pre_gemm(const BackwardArgs& b, hipStream_t stream) {
     const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
     unrotate_kernel<BF16><<<dim3(blocks), dim3(256), 0, stream>>>(b);
   }
-  activations_kernel<BF16><<<dim3((b.T + 3) / 4), dim3(256), 0, stream>>>(b);
+  const dim3 rows((b.T + 3) / 4), threads(256);
+  switch (b.H) {
+    case 1024: activations_kernel<BF16, 2><<<rows, threads, 0, stream>>>(b); break;
+    case 2048: activations_kernel<BF16, 4><<<rows, threads, 0, stream>>>(b); break;
+    case 4096: activations_kernel<BF16, 8><<<rows, threads, 0, stream>>>(b); break;
+    default: activations_kernel<BF16, 0><<<rows, threads, 0, stream>>>(b); break;
+  }
   if (b.dbias) return colsum<BF16, 0>(b, b.N, b.dbias, stream);
   return hipGetLastError();
 }
 
 template <bool BF16>
 hipError_t post_gemm(const BackwardArgs& b, hipStream_t stream) {
-  norm_grad_kernel<BF16><<<dim3((b.T + 3) / 4), dim3(256), 0, stream>>>(b);
+  const dim3 rows((b.T + 3) / 4), threads(256);
+  switch (b.H) {
+    case 1024: norm_grad_kernel<BF16, 2><<<rows, threads, 0, stream>>>(b); break;
+    case 2048: norm_grad_kernel<BF16, 4><<<rows, threads, 0, stream>>>(b); break;
+    case 4096: norm_grad_kernel<BF16, 8><<<rows, threads, 0, stream>>>(b); break;
+    default: norm_grad_kernel<BF16, 0><<<rows, threads, 0, stream>>>(b); break;
+  }
   return colsum<BF16, 1>(b, b.H, b.dw_norm, stream);
 }
 
