@@ -399,3 +399,34 @@ def test_variant_names():
                 assert v == "decode"
             else:
                 assert v == "prefill"
+
+
+@pytest.mark.parametrize("cid,T", [(3, 300), (4, 100)])
+def test_graph_replays(cid, T):
+    """A forward captured in a HIP graph (split-K prefill, decode over two chunks): each of
+    several replays, with eager forwards of other inputs in between, writes exactly the
+    eager result; the kernels leave their arrival counters at zero for the next call."""
+    wl = workloads.WORKLOADS[cid].with_tokens(1, T) if cid == 3 else workloads.WORKLOADS[cid].with_tokens(T, 1)
+    inp = workloads.make_inputs(wl, seed=31 + T)
+    other = workloads.make_inputs(wl, seed=97 + T)
+    dev = lambda i: (i["x"].to(DEV), i["w_norm"].to(DEV), i["w_qkv"].to(DEV),
+                     None if i["bias"] is None else i["bias"].to(DEV), i["pos"].to(DEV))
+    args, args2 = dev(inp), dev(other)
+    with qkv.Plan.for_workload(wl) as plan:
+        assert plan.variant(T) == ("prefill_split" if cid == 3 else "decode")
+        ref = [t.clone() for t in plan.forward(*args)]
+        out = plan.forward(*args)
+        stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            plan.forward(*args, out=out, stream=stream)
+        for i in range(4):
+            for t in out:
+                t.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            for name, g, r in zip("QKV", out, ref):
+                assert torch.equal(g, r), f"replay {i}: {name} differs from the eager forward"
+            plan.forward(*args2)  # eager work between replays
+            torch.cuda.synchronize()
