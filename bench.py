@@ -333,7 +333,7 @@ def other_workloads_leg(qkv, workloads, skip: str, steps: int = 30, warmup: int 
         elif wl.dtype == "bf16":
             entry["timing"] = "weight warm in the last-level cache (see the decode object for HBM-cold)"
         else:
-            entry["timing"] = "launch-bound (two launches: row reduction and fp32 kernel)"
+            entry["timing"] = "launch-bound (one fp32 kernel with the row reduction fused in)"
         res[wl.name] = entry
         del bufs
         torch.cuda.empty_cache()

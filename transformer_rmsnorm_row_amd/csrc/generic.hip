@@ -5,9 +5,11 @@
 //
 // What it computes follows the fused-kernel listing of the page "Liger-Kernel底层优化：
 // 新一代内核级推理加速引擎介绍" (section "融合内核是如何工作的？来看一段简化版实现"):
-// each input element enters the dot products already scaled by the token's inverse
-// RMS and the norm weight (the normalised row never goes to memory), the bias is
-// added to each dot product, and the rotation pairs feature i with i + head_dim/2.
+// each input element enters the dot products scaled by the norm weight, the token's
+// sum of squares is gathered from the same staged values and its inverse RMS scales
+// the dot products (the normalised row never goes to memory, and no separate pass
+// over x is needed), the bias is added to each dot product, and the rotation pairs
+// feature i with i + head_dim/2.
 // Unlike the listing (one thread per output feature re-reading the whole row and
 // weight column), a 256-thread block computes a 32-token x 32-pair tile from LDS:
 // each thread owns 4 tokens x one rotation pair (columns c and c + head_dim/2), so
@@ -59,17 +61,24 @@ __global__ __launch_bounds__(256) void generic_kernel(ForwardArgs a) {
   float acc[4][2];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j][0] = acc[j][1] = 0.f;
+  // sums of squares of the raw x values this thread stages (rows tid / 32 + 8 m); 1/rms
+  // scales the accumulators in the epilogue: diag(r) (X diag(w)) W = (diag(r) X diag(w)) W
+  float ssq[4] = {0.f, 0.f, 0.f, 0.f};
 
   for (int k0 = 0; k0 < a.H; k0 += BK) {
-    // A slice: a[t,k] = x[t,k] * inv_rms[t] * w_norm[k], 32 x 32, 4 per thread.
+    // A slice: x[t,k] * w_norm[k], 32 x 32, 4 per thread (row tid / 32 + 8 m, column
+    // tid % 32), and the squares of x into the row sums.
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       int e = tid + 256 * m;
       int r = e / BK, cc = e % BK;
       int t = t0 + r, kk = k0 + cc;
-      float val = 0.f;
-      if (t < a.T && kk < a.H)
-        val = load_elem<BF16>(a.x, (size_t)t * a.H + kk) * a.inv_rms[t] * load_elem<BF16>(a.w_norm, kk);
+      float xv = 0.f, val = 0.f;
+      if (t < a.T && kk < a.H) {
+        xv = load_elem<BF16>(a.x, (size_t)t * a.H + kk);
+        val = xv * load_elem<BF16>(a.w_norm, kk);
+      }
+      ssq[m] = fmaf(xv, xv, ssq[m]);
       As[cc][r] = val;
     }
     // B slice: the two columns of each pair, 32 x 64, 8 per thread.
@@ -99,6 +108,17 @@ __global__ __launch_bounds__(256) void generic_kernel(ForwardArgs a) {
     __syncthreads();
   }
 
+  // 1/rms of the block's 32 rows: the 32 lanes staging a row add their sums
+  __shared__ float s_rinv[BT];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float v = ssq[m];
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off, 32);
+    if ((tid & 31) == 0) s_rinv[tid / 32 + 8 * m] = rsqrtf(v / (float)a.H + a.eps);
+  }
+  __syncthreads();
+
   const int u = u0 + tx;
   if (u >= units) return;
   const int c = pair_col(u, half, a.d);
@@ -125,7 +145,8 @@ __global__ __launch_bounds__(256) void generic_kernel(ForwardArgs a) {
   for (int j = 0; j < 4; ++j) {
     int t = t0 + ty * 4 + j;
     if (t >= a.T) break;
-    float y0 = acc[j][0] + b0, y1 = acc[j][1] + b1;
+    const float rinv = s_rinv[ty * 4 + j];
+    float y0 = fmaf(acc[j][0], rinv, b0), y1 = fmaf(acc[j][1], rinv, b1);
     if (rotate) {
       float cs, sn;
       rope_cos_sin(a.pos[t], rev, cs, sn);
@@ -147,8 +168,6 @@ __global__ __launch_bounds__(256) void generic_kernel(ForwardArgs a) {
 }  // namespace
 
 hipError_t launch_generic(const ForwardArgs& a, hipStream_t stream) {
-  hipError_t e = launch_inv_rms(a.x, a.inv_rms, a.T, a.H, a.eps, a.bf16, stream);
-  if (e != hipSuccess) return e;
   dim3 grid((a.T + BT - 1) / BT, (a.N / 2 + BU - 1) / BU), block(256);
   if (a.bf16)
     generic_kernel<true><<<grid, block, 0, stream>>>(a);
