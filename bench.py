@@ -17,7 +17,8 @@ line carries:
   decode        the 64-token decode step streaming its weight from HBM (8 weight
                 copies rotated so the 256 MB last-level cache cannot hold them);
   other_workloads  every other forward workload (tiny fp32, Llama-3-8B GQA prefill,
-                the decode step warm, Qwen-7B prefill with bias) at full size;
+                the decode step warm, Qwen-7B prefill with bias) at full size, and
+                two mid-size batches (512 tokens on the GQA shape, 128 decode tokens);
   prefill_zero_weight  the headline forward with an all-zero weight, a labelled
                 diagnostic: how much of the prefill time is the clock lost to the
                 matrix cores' power draw on random operands;
@@ -315,7 +316,12 @@ def other_workloads_leg(qkv, workloads, skip: str, steps: int = 30, warmup: int 
     cold)."""
     import torch
     res = {}
-    for wl in workloads.WORKLOADS.values():
+    # the five workloads, then two mid-size batches on their shapes: 512 tokens of the GQA
+    # prefill shape (the prefill kernel's split-K form) and 128 sequences of the decode step
+    # (the decode kernel over two 64-token chunks)
+    extra = [workloads.BY_NAME["llama3_8b_gqa_prefill"].with_tokens(1, 512),
+             workloads.BY_NAME["gqa_decode"].with_tokens(128, 1)]
+    for wl in list(workloads.WORKLOADS.values()) + extra:
         if wl.name == skip:
             continue
         inp = workloads.make_inputs(wl)
