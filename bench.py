@@ -318,7 +318,7 @@ def other_workloads_leg(qkv, workloads, skip: str, steps: int = 30, warmup: int 
     res = {}
     # the five workloads, then two mid-size batches on their shapes: 512 tokens of the GQA
     # prefill shape (the prefill kernel's split-K form) and 128 sequences of the decode step
-    # (the decode kernel over two 64-token chunks)
+    # (one launch of the decode kernel's 128-token form)
     extra = [workloads.BY_NAME["llama3_8b_gqa_prefill"].with_tokens(1, 512),
              workloads.BY_NAME["gqa_decode"].with_tokens(128, 1)]
     for wl in list(workloads.WORKLOADS.values()) + extra:

@@ -72,7 +72,7 @@ typedef enum qkv_variant {
   QKV_VARIANT_GENERIC = 0,  /* fp32 FMA tiles: any supported shape, both dtypes        */
   QKV_VARIANT_PREFILL = 1,  /* bf16 MFMA GEMM, norm-on-load, rotary epilogue           */
   QKV_VARIANT_DECODE = 2,   /* bf16 MFMA weight-streaming kernel for small token counts:
-                               up to 256 tokens, one launch per 64-token chunk          */
+                               up to 192 (or 256) tokens, one launch per 128 tokens     */
   QKV_VARIANT_PREFILL_SPLIT = 3  /* the prefill kernel with the hidden dimension split over
                                two workgroups per tile, when the tiles alone would leave
                                at least half of the CUs idle                            */
@@ -207,9 +207,10 @@ qkv_status qkv_swiglu_forward(int64_t num_tokens, int32_t hidden, int32_t interm
                               void* out, void* stream);
 
 /* Which variant a forward of num_tokens tokens runs on, in *variant (a qkv_variant):
- * bf16 plans of a shape the decode kernel supports take it up to 256 tokens (as
- * consecutive launches of up to 64 tokens, queued in order on the forward's stream),
- * other bf16 plans of a supported shape the prefill kernel -- in its split form
+ * bf16 plans of a shape the decode kernel supports take it up to 192 tokens, or up to
+ * 256 when the prefill kernel has no split form for T (as consecutive launches of up
+ * to 128 tokens, queued in order on the forward's stream); other bf16 plans of a
+ * supported shape take the prefill kernel -- in its split form
  * (QKV_VARIANT_PREFILL_SPLIT) when T's 256 x 256 tiles number at most 128 and the
  * hidden size divides into two slices of a multiple of 4 steps of 32, at least 8 --
  * everything else generic.

@@ -357,11 +357,12 @@ def test_decode_shapes(hidden, nq, nkv, bias):
     P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], wl.name)
 
 
-@pytest.mark.parametrize("T", [65, 100, 128, 191, 256])
+@pytest.mark.parametrize("T", [65, 100, 128, 150, 191, 192])
 def test_decode_in_chunks(T):
-    """65 to 256 tokens run the decode kernel once per 64-token chunk (fewer than a
+    """65 to 192 tokens run the decode kernel once per 128-token chunk (fewer than a
     prefill tile's 256 rows would leave most compute units idle); full comparison with
-    the oracle, and each chunk's rows bit for bit equal to a forward of that chunk alone."""
+    the oracle, and every 64 rows bit for bit equal to a forward of those 64 tokens alone
+    (which the kernel's 64-token form computes)."""
     wl = workloads.WORKLOADS[4].with_tokens(T, 1)
     inp = workloads.make_inputs(wl, seed=700 + T)
     with qkv.Plan.for_workload(wl) as plan:
@@ -376,15 +377,30 @@ def test_decode_in_chunks(T):
 
 
 def test_decode_chunk_boundary():
-    """The decode kernel serves up to 256 tokens of a plan; 257 go to the prefill kernel
-    (in its split-K form while the tiles number at most 128: 24 per 256 tokens here)."""
+    """The decode kernel serves up to 192 tokens of a plan whose prefill kernel has a split-K
+    form (a 128-token launch, then one of the 64-token form); from 193 on, the split-K
+    prefill (while the tiles number at most 128: 24 per 256 tokens here)."""
     wl = workloads.WORKLOADS[4].with_tokens(1537, 1)
     with qkv.Plan.for_workload(wl) as plan:
-        assert plan.variant(256) == "decode"
-        assert plan.variant(257) == "prefill_split"
+        assert plan.variant(192) == "decode"
+        assert plan.variant(193) == "prefill_split"
         assert plan.variant(1280) == "prefill_split"   # 5 x 24 = 120 tiles
         assert plan.variant(1281) == "prefill"         # 6 x 24 = 144 tiles
         assert plan.variant(1) == "decode"
+
+
+def test_decode_two_full_chunks():
+    """Without a split-K prefill (hidden 1152: 36 steps of 32 do not split into two multiples
+    of 4) the decode kernel keeps up to 256 tokens, two launches of its 128-token form; full
+    comparison with the oracle at 256, and 257 goes to the plain prefill kernel."""
+    wl = workloads.Workload(10, "decode_1152_8x2", 256, 1, 1152, 8, 2, 128, True, 1e4, 1e-6,
+                            "bf16", "uniform32768")
+    inp = workloads.make_inputs(wl, seed=1152)
+    with qkv.Plan.for_workload(wl.with_tokens(257, 1)) as plan:
+        assert plan.variant(256) == "decode"
+        assert plan.variant(257) == "prefill"
+        got = run(plan, inp)
+    P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], wl.name)
 
 
 def test_variant_names():
@@ -401,11 +417,12 @@ def test_variant_names():
                 assert v == "prefill"
 
 
-@pytest.mark.parametrize("cid,T", [(3, 300), (4, 100)])
+@pytest.mark.parametrize("cid,T", [(3, 300), (4, 150)])
 def test_graph_replays(cid, T):
-    """A forward captured in a HIP graph (split-K prefill, decode over two chunks): each of
-    several replays, with eager forwards of other inputs in between, writes exactly the
-    eager result; the kernels leave their arrival counters at zero for the next call."""
+    """A forward captured in a HIP graph (split-K prefill; decode over a 128-token and a
+    22-token chunk): each of several replays, with eager forwards of other inputs in
+    between, writes exactly the eager result; the kernels leave their arrival counters at
+    zero for the next call."""
     wl = workloads.WORKLOADS[cid].with_tokens(1, T) if cid == 3 else workloads.WORKLOADS[cid].with_tokens(T, 1)
     inp = workloads.make_inputs(wl, seed=31 + T)
     other = workloads.make_inputs(wl, seed=97 + T)

@@ -80,9 +80,9 @@ int prefill_split_units(int max_tokens, int N);
 // plan whose split scratch holds `units` partial tiles.
 int prefill_split_count(int T, int H, int N, int units);
 size_t prefill_split_floats(int units);
-// Token capacity of one decode launch; larger batches run as consecutive launches of
-// up to this many tokens.
-constexpr int kDecodeTokens = 64;
+// Token capacity of one decode launch (batches of up to 64 tokens run a 64-token form
+// of the kernel); larger batches run as consecutive launches of up to this many tokens.
+constexpr int kDecodeTokens = 128;
 hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
 // gated MLP on the prefill kernel: x, w_norm, w = [H, 2I] (gate | up), q = out [T, I],
 // N = 2I, T, H, eps, bf16

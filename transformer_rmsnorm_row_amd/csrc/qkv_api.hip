@@ -129,20 +129,23 @@ qkv_status ensure_backward_scratch(Plan* pl) {
   return QKV_OK;
 }
 
-// Up to this many tokens the decode kernel, run over consecutive chunks of
-// kDecodeTokens, is faster than the prefill kernel, whose few 256 x 256 tiles then
-// leave most compute units idle while each walks the whole hidden dimension.
-constexpr int64_t kDecodeMaxTokens = 4 * qkv::kDecodeTokens;
+// Token counts the decode kernel takes, run over consecutive chunks of kDecodeTokens.
+// The prefill kernel's few 256 x 256 tiles leave most compute units idle at these
+// sizes, each walking the whole hidden dimension.  Its split-K form doubles the
+// workgroups, and on the GQA decode shape it overtakes two decode launches once the
+// second launch needs the 128-token form (193+ tokens); without a split form the decode
+// kernel keeps up to two full 128-token launches.
+constexpr int64_t kDecodeMaxTokens = qkv::kDecodeTokens + 64;
+constexpr int64_t kDecodeMaxTokensUnsplit = 2 * qkv::kDecodeTokens;
 
 int choose_variant(const Plan* pl, int64_t T) {
-  if (pl->bf16 && pl->decode_ok && T <= kDecodeMaxTokens &&
+  const bool split = pl->bf16 && pl->prefill_ok && pl->kpart &&
+                     qkv::prefill_split_count((int)T, pl->desc.hidden, pl->N, pl->kpart_units) > 1;
+  if (pl->bf16 && pl->decode_ok && T <= (split ? kDecodeMaxTokens : kDecodeMaxTokensUnsplit) &&
       qkv::decode_supports((int)std::min<int64_t>(T, qkv::kDecodeTokens), pl->desc.hidden, pl->N, pl->Nq, pl->Nkv,
                            pl->desc.head_dim))
     return QKV_VARIANT_DECODE;
-  if (pl->bf16 && pl->prefill_ok)
-    return pl->kpart && qkv::prefill_split_count((int)T, pl->desc.hidden, pl->N, pl->kpart_units) > 1
-               ? QKV_VARIANT_PREFILL_SPLIT
-               : QKV_VARIANT_PREFILL;
+  if (pl->bf16 && pl->prefill_ok) return split ? QKV_VARIANT_PREFILL_SPLIT : QKV_VARIANT_PREFILL;
   return QKV_VARIANT_GENERIC;
 }
 
