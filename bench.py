@@ -19,6 +19,8 @@ line carries:
   other_workloads  every other forward workload (tiny fp32, Llama-3-8B GQA prefill,
                 the decode step warm, Qwen-7B prefill with bias) at full size, and
                 two mid-size batches (512 tokens on the GQA shape, 128 decode tokens);
+  unfused       the chain as three steps (RMSNorm kernel, rocBLAS GEMM, bias+RoPE
+                kernel) against the fused forward, on the prefill and decode shapes;
   prefill_zero_weight  the headline forward with an all-zero weight, a labelled
                 diagnostic: how much of the prefill time is the clock lost to the
                 matrix cores' power draw on random operands;
@@ -283,6 +285,58 @@ def backward_leg(qkv, workloads, wl, bufs, steps: int = 10, warmup: int = 2):
                     "sums in this library's kernels"}
 
 
+def _event_time(fn, steps: int, warmup: int) -> float:
+    """Seconds per call of fn, HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps
+
+
+def unfused_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
+    """The chain as three separate steps (RMSNorm kernel -> rocBLAS GEMM -> bias+RoPE
+    kernel, qkv_forward_unfused) against the fused forward, on the headline prefill
+    shape and on the decode step (weight warm in the last-level cache for both), with
+    the two unfused kernels also timed alone.  Algorithmic HBM bytes: fused = x + W +
+    Q/K/V once; unfused adds xn written and read back, and y read and written again by
+    the rotation."""
+    import torch
+    res = {}
+    for name in ("llama7b_prefill", "gqa_decode"):
+        wl = workloads.BY_NAME[name]
+        x, w, W, b, pos, q, k, v = device_inputs(wl, workloads.make_inputs(wl))
+        plan = qkv.Plan.for_workload(wl)
+        _, bufs = plan.forward_unfused(x, w, W, b, pos)
+        xn, y = bufs
+        fused = _event_time(lambda: plan.forward(x, w, W, b, pos, out=(q, k, v)), steps, warmup)
+        unfused = _event_time(lambda: plan.forward_unfused(x, w, W, b, pos, out=bufs), steps, warmup)
+        norm = _event_time(lambda: plan.rms_norm(x, w, out=xn), steps, warmup)
+        rope = _event_time(lambda: plan.rope(y, b, pos), steps, warmup)
+        plan.close()
+        T, H, N, e = wl.tokens, wl.hidden, wl.n_total, 2
+        fused_bytes = wl.algorithmic_bytes()
+        unfused_bytes = fused_bytes + 2 * T * H * e + 2 * T * N * e
+        res[name] = {"tokens": T, "fused_us": round(fused * 1e6, 2), "unfused_us": round(unfused * 1e6, 2),
+                     "unfused_over_fused": round(unfused / fused, 3),
+                     "rms_norm_us": round(norm * 1e6, 2), "rope_us": round(rope * 1e6, 2),
+                     "gemm_us_by_difference": round((unfused - norm - rope) * 1e6, 2),
+                     "rms_norm_hbm_GBps": round(2 * T * H * e / norm / 1e9, 1),
+                     "rope_hbm_GBps": round(2 * T * N * e / rope / 1e9, 1),
+                     "algorithmic_bytes_fused": fused_bytes, "algorithmic_bytes_unfused": unfused_bytes,
+                     "kernels": "fused: 1 launch; unfused: norm kernel, rocBLAS GEMM, rotation kernel"}
+        del x, w, W, b, pos, q, k, v, xn, y, bufs
+        torch.cuda.empty_cache()
+    return res
+
+
 def swiglu_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
     """The gated-MLP forward (RMSNorm, gate|up GEMM, SiLU(g) * u) on the Llama-7B MLP
     shape, timed with HIP events on the current stream."""
@@ -505,6 +559,8 @@ def main() -> int:
         out["backward"] = backward_leg(qkv, workloads, wl, bufs)
         del bufs
         torch.cuda.empty_cache()
+        print("[bench] unfused comparison leg", file=sys.stderr, flush=True)
+        out["unfused"] = unfused_leg(qkv, workloads)
         print("[bench] other workloads leg", file=sys.stderr, flush=True)
         out["other_workloads"] = other_workloads_leg(qkv, workloads, skip=wl.name)
     if not args.no_cpu_baseline:

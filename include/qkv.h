@@ -148,6 +148,40 @@ qkv_status qkv_forward_kv_cache(qkv_plan plan, int64_t num_tokens,
 qkv_status qkv_rms_inv(qkv_plan plan, int64_t num_tokens, const void* x,
                        float* inv_rms, void* stream);
 
+/* The chain's steps unfused, for measuring what the fusion saves.  The pages on
+ * Liger-Kernel credit fusing RMSNorm, the projection and RoPE with fewer launches and
+ * fewer HBM round trips (page "Liger-Kernel底层优化：新一代内核级推理加速引擎介绍", the
+ * sections on why fusion pays and on the fused kernel).  These entry points run the same arithmetic as
+ * separate kernels, each reading its input from and writing its output to HBM.
+ * Same plan, argument rules (dtype, alignment to 16 bytes, 4 for pos), asynchrony and
+ * errors as qkv_forward.
+ *
+ * qkv_rms_norm: xn [T, H] = x[t,k] * 1/sqrt(mean_k x[t,k]^2 + eps) * w_norm[k] (the
+ *   fused chain's normalised activations, computed in fp32, rounded once to the plan
+ *   dtype), into the caller's buffer xn. */
+qkv_status qkv_rms_norm(qkv_plan plan, int64_t num_tokens, const void* x, const void* w_norm,
+                        void* xn, void* stream);
+
+/* qkv_rope: in place on a projection output y [T, N] laid out like the fused forward's
+ * outputs side by side (columns: the Q heads, then K, then V): adds bias [N] to every
+ * column (exactly when the plan has has_bias = 1; NULL otherwise), then turns each
+ * rotate-half pair (i, i + head_dim/2) of every Q and K head by pos[t] * theta^(-2i/d)
+ * radians, as the fused forward does; V gets only the bias. */
+qkv_status qkv_rope(qkv_plan plan, int64_t num_tokens, const void* bias, const int32_t* pos,
+                    void* y, void* stream);
+
+/* qkv_forward_unfused: the whole chain as three steps -- qkv_rms_norm into the caller's
+ * xn [T, H], the projection y = xn W_qkv as a rocBLAS GEMM (fp32 accumulation, output in
+ * the plan dtype) into the caller's y [T, N], then qkv_rope on y.  Q, K and V are the
+ * column blocks [0, nq*d), [nq*d, (nq+nkv)*d) and the rest of y.  Each step rounds its
+ * output to the plan dtype, so results differ from qkv_forward's by those roundings.
+ * The first call on a plan creates its GEMM library handle (host allocation and device
+ * memory; not under graph capture). */
+qkv_status qkv_forward_unfused(qkv_plan plan, int64_t num_tokens,
+                               const void* x, const void* w_norm, const void* w_qkv,
+                               const void* bias, const int32_t* pos,
+                               void* xn, void* y, void* stream);
+
 /* Backward of the chain: given the gradients dq [T, nq*head_dim], dk and dv
  * [T, nkv*head_dim] of a loss with respect to Q, K and V, write its gradients with
  * respect to the inputs:

@@ -88,6 +88,9 @@ def test_null_pointers_rejected():
     assert lib.qkv_rms_inv(None, 4, None, None, None) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_forward_kv_cache(None, 4, *([None] * 6), 16, None, None, None, None) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_backward(None, 4, *([None] * 11), None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_rms_norm(None, 4, None, None, None, None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_rope(None, 4, None, None, None, None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_forward_unfused(None, 4, *([None] * 7), None) == qkv.QKV_ERR_INVALID_ARG
     v = ctypes.c_int32()
     assert lib.qkv_plan_variant(None, 4, ctypes.byref(v)) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_plan_destroy(None) == qkv.QKV_OK
@@ -100,6 +103,10 @@ def test_unknown_handle_rejected():
     assert lib.qkv_forward(ctypes.cast(fake, ctypes.c_void_p), 1, *([None] * 8), None) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_forward_kv_cache(ctypes.cast(fake, ctypes.c_void_p), 1, *([None] * 6), 16,
                                     None, None, None, None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_rms_norm(ctypes.cast(fake, ctypes.c_void_p), 1, None, None, None, None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_rope(ctypes.cast(fake, ctypes.c_void_p), 1, None, None, None, None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_forward_unfused(ctypes.cast(fake, ctypes.c_void_p), 1, *([None] * 7),
+                                   None) == qkv.QKV_ERR_INVALID_ARG
 
 
 def test_valid_descriptor_without_gpu():

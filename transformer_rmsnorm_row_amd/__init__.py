@@ -32,6 +32,9 @@ EXPORTS = {
     "qkv_swiglu_forward": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_double, _vp, _vp, _vp, _vp, _vp]),
     "qkv_rms_inv": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp]),
+    "qkv_rms_norm": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp]),
+    "qkv_rope": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp]),
+    "qkv_forward_unfused": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qkv_plan_variant": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)]),
     "qkv_plan_destroy": (ctypes.c_int, [_vp]),
     "qkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -278,6 +281,59 @@ class Plan:
         self._check_tensor(out, "inv_rms", (T,), torch.float32)
         _check(self._lib.qkv_rms_inv(self.handle, T, _ptr(x), _ptr(out), _stream_handle(stream)), "qkv_rms_inv")
         return out
+
+    def rms_norm(self, x: torch.Tensor, w_norm: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """The normalised activations [T, H] alone (qkv_rms_norm)."""
+        T = x.shape[0]
+        self._check_tensor(x, "x", (T, self.hidden), self.dtype)
+        self._check_tensor(w_norm, "w_norm", (self.hidden,), self.dtype)
+        if out is None:
+            out = torch.empty_like(x)
+        self._check_tensor(out, "xn", (T, self.hidden), self.dtype)
+        _check(self._lib.qkv_rms_norm(self.handle, T, _ptr(x), _ptr(w_norm), _ptr(out), _stream_handle(stream)),
+               "qkv_rms_norm")
+        return out
+
+    def rope(self, y: torch.Tensor, bias: Optional[torch.Tensor], pos: torch.Tensor,
+             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """Bias and rotation applied in place to a projection output y [T, N] (qkv_rope)."""
+        T = y.shape[0]
+        N = self.n_q + 2 * self.n_kv
+        self._check_tensor(y, "y", (T, N), self.dtype)
+        if bias is not None:
+            self._check_tensor(bias, "bias", (N,), self.dtype)
+        self._check_tensor(pos, "pos", (T,), torch.int32)
+        _check(self._lib.qkv_rope(self.handle, T, _ptr(bias), _ptr(pos), _ptr(y), _stream_handle(stream)),
+               "qkv_rope")
+        return y
+
+    def forward_unfused(self, x: torch.Tensor, w_norm: torch.Tensor, w_qkv: torch.Tensor,
+                        bias: Optional[torch.Tensor], pos: torch.Tensor,
+                        out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                        stream: Optional[torch.cuda.Stream] = None):
+        """The chain as three steps (qkv_forward_unfused); returns (q, k, v) as column
+        views of y [T, N], plus (xn, y) for reuse as ``out``."""
+        T = x.shape[0]
+        H, N = self.hidden, self.n_q + 2 * self.n_kv
+        self._check_tensor(x, "x", (T, H), self.dtype)
+        self._check_tensor(w_norm, "w_norm", (H,), self.dtype)
+        self._check_tensor(w_qkv, "w_qkv", (H, N), self.dtype)
+        if bias is not None:
+            self._check_tensor(bias, "bias", (N,), self.dtype)
+        self._check_tensor(pos, "pos", (T,), torch.int32)
+        if out is None:
+            xn = torch.empty((T, H), dtype=self.dtype, device=x.device)
+            y = torch.empty((T, N), dtype=self.dtype, device=x.device)
+        else:
+            xn, y = out
+            self._check_tensor(xn, "xn", (T, H), self.dtype)
+            self._check_tensor(y, "y", (T, N), self.dtype)
+        st = self._lib.qkv_forward_unfused(self.handle, T, _ptr(x), _ptr(w_norm), _ptr(w_qkv), _ptr(bias),
+                                           _ptr(pos), _ptr(xn), _ptr(y), _stream_handle(stream))
+        _check(st, "qkv_forward_unfused")
+        nq, nkv = self.n_q, self.n_kv
+        return (y[:, :nq], y[:, nq:nq + nkv], y[:, nq + nkv:]), (xn, y)
 
     def close(self) -> None:
         if self._handle is not None:

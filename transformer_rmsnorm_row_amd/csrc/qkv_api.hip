@@ -13,6 +13,7 @@
 
 #include "qkv.h"
 #include "launch.h"
+#include "unfused.h"
 
 namespace {
 
@@ -38,7 +39,7 @@ struct Plan {
   void* bwd_act;        // [max_tokens, H] plan dtype
   float* bwd_ga;        // [max_tokens, H] fp32
   float* bwd_partial;   // [kBackwardChunks, max(N, H)] fp32
-  rocblas_handle blas;  // the two GEMMs of the backward
+  rocblas_handle blas;  // the two GEMMs of the backward, the unfused forward's GEMM
 };
 
 std::mutex g_mu;
@@ -109,24 +110,37 @@ void free_scratch(Plan* pl) {
   pl->blas = nullptr;
 }
 
+// The GEMM library handle, created on the first call that needs it.
+qkv_status ensure_blas_locked(Plan* pl) {
+  if (pl->blas) return QKV_OK;
+  rocblas_handle h = nullptr;
+  if (rocblas_create_handle(&h) != rocblas_status_success) return QKV_ERR_HIP;
+  pl->blas = h;
+  return QKV_OK;
+}
+
+qkv_status ensure_blas(Plan* pl) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return ensure_blas_locked(pl);
+}
+
 // First backward through a plan: its scratch and the GEMM library handle.
 qkv_status ensure_backward_scratch(Plan* pl) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (pl->blas) return QKV_OK;
+  if (pl->bwd_partial) return ensure_blas_locked(pl);
   const size_t T = (size_t)pl->desc.max_tokens, H = (size_t)pl->desc.hidden, N = (size_t)pl->N;
   const size_t elem = pl->bf16 ? 2 : 4;
   const size_t widest = N > H ? N : H;
-  bool ok = hipMalloc(&pl->bwd_gy, T * N * elem) == hipSuccess && hipMalloc(&pl->bwd_act, T * H * elem) == hipSuccess &&
-            hipMalloc(&pl->bwd_ga, T * H * sizeof(float)) == hipSuccess &&
+  // each buffer is allocated once: a call after a failed allocation keeps what succeeded
+  bool ok = (pl->bwd_gy || hipMalloc(&pl->bwd_gy, T * N * elem) == hipSuccess) &&
+            (pl->bwd_act || hipMalloc(&pl->bwd_act, T * H * elem) == hipSuccess) &&
+            (pl->bwd_ga || hipMalloc(&pl->bwd_ga, T * H * sizeof(float)) == hipSuccess) &&
             hipMalloc(&pl->bwd_partial, (size_t)qkv::kBackwardChunks * widest * sizeof(float)) == hipSuccess;
   if (!ok) {
     (void)hipGetLastError();
     return QKV_ERR_OUT_OF_MEMORY;
   }
-  rocblas_handle h = nullptr;
-  if (rocblas_create_handle(&h) != rocblas_status_success) return QKV_ERR_HIP;
-  pl->blas = h;
-  return QKV_OK;
+  return ensure_blas_locked(pl);
 }
 
 // Token counts the decode kernel takes, run over consecutive chunks of kDecodeTokens.
@@ -341,6 +355,67 @@ qkv_status qkv_rms_inv(qkv_plan plan, int64_t num_tokens, const void* x, float* 
   if (st != QKV_OK) return st;
   hipError_t e = qkv::launch_inv_rms(x, inv_rms, (int)num_tokens, pl->desc.hidden, (float)pl->desc.eps, pl->bf16,
                                      reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
+}
+
+qkv_status qkv_rms_norm(qkv_plan plan, int64_t num_tokens, const void* x, const void* w_norm, void* xn,
+                        void* stream) {
+  Plan* pl = as_plan(plan);
+  if (!pl) return QKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return QKV_OK;
+  if (num_tokens < 0 || num_tokens > pl->desc.max_tokens) return QKV_ERR_INVALID_ARG;
+  if (!x || !w_norm || !xn || !aligned(x, 16) || !aligned(w_norm, 16) || !aligned(xn, 16)) return QKV_ERR_INVALID_ARG;
+  qkv_status st = check_device(pl);
+  if (st != QKV_OK) return st;
+  const hipError_t e = qkv::launch_rms_norm(x, w_norm, xn, (int)num_tokens, pl->desc.hidden, (float)pl->desc.eps,
+                                            pl->bf16, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
+}
+
+qkv_status qkv_rope(qkv_plan plan, int64_t num_tokens, const void* bias, const int32_t* pos, void* y, void* stream) {
+  Plan* pl = as_plan(plan);
+  if (!pl) return QKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return QKV_OK;
+  if (num_tokens < 0 || num_tokens > pl->desc.max_tokens) return QKV_ERR_INVALID_ARG;
+  if ((bias != nullptr) != (pl->desc.has_bias == 1)) return QKV_ERR_INVALID_ARG;
+  if (!pos || !y || !aligned(pos, 4) || !aligned(y, 16) || (bias && !aligned(bias, 16))) return QKV_ERR_INVALID_ARG;
+  qkv_status st = check_device(pl);
+  if (st != QKV_OK) return st;
+  const hipError_t e = qkv::launch_rope(y, bias, pos, pl->rev_freq, (int)num_tokens, pl->N, pl->Nq, pl->Nkv,
+                                        pl->desc.head_dim, pl->bf16, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
+}
+
+qkv_status qkv_forward_unfused(qkv_plan plan, int64_t num_tokens, const void* x, const void* w_norm,
+                               const void* w_qkv, const void* bias, const int32_t* pos, void* xn, void* y,
+                               void* stream) {
+  Plan* pl = as_plan(plan);
+  if (!pl) return QKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return QKV_OK;
+  if (num_tokens < 0 || num_tokens > pl->desc.max_tokens) return QKV_ERR_INVALID_ARG;
+  if ((bias != nullptr) != (pl->desc.has_bias == 1)) return QKV_ERR_INVALID_ARG;
+  if (!x || !w_norm || !w_qkv || !pos || !xn || !y) return QKV_ERR_INVALID_ARG;
+  for (const void* p : {x, w_norm, w_qkv, (const void*)xn, (const void*)y})
+    if (!aligned(p, 16)) return QKV_ERR_INVALID_ARG;
+  if (!aligned(pos, 4) || (bias && !aligned(bias, 16))) return QKV_ERR_INVALID_ARG;
+  qkv_status st = check_device(pl);
+  if (st != QKV_OK) return st;
+  st = ensure_blas(pl);
+  if (st != QKV_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int T = (int)num_tokens, H = pl->desc.hidden, N = pl->N;
+  if (qkv::launch_rms_norm(x, w_norm, xn, T, H, (float)pl->desc.eps, pl->bf16, s) != hipSuccess) return QKV_ERR_HIP;
+  // Row-major y [T, N] = xn [T, H] W [H, N]  <=>  column-major (N x T) = W (N x H) * xn (H x T),
+  // fp32 accumulation, output in the plan dtype.
+  if (rocblas_set_stream(pl->blas, s) != rocblas_status_success) return QKV_ERR_HIP;
+  const rocblas_datatype io = pl->bf16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+  const float one = 1.0f, zero = 0.0f;
+  if (rocblas_gemm_ex(pl->blas, rocblas_operation_none, rocblas_operation_none, N, T, H, &one, w_qkv, io, N, xn, io,
+                      H, &zero, y, io, N, y, io, N, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0,
+                      0) != rocblas_status_success)
+    return QKV_ERR_HIP;
+  const hipError_t e =
+      qkv::launch_rope(y, bias, pos, pl->rev_freq, T, N, pl->Nq, pl->Nkv, pl->desc.head_dim, pl->bf16, s);
   return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
 }
 
