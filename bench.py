@@ -47,8 +47,9 @@ COUNTER_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
 
 # sources each kernel is built from: a counter reading stays valid while these are unchanged
+# (the plain prefill forward is the pre-pass of rownorm.hip, then prefill_kernel)
 KERNEL_SOURCES = {
-    "prefill_kernel": ("prefill.hip", "device_common.h", "launch.h"),
+    "prefill_kernel": ("prefill.hip", "rownorm.hip", "device_common.h", "launch.h"),
     "decode_kernel": ("decode.hip", "device_common.h", "launch.h"),
 }
 
@@ -63,9 +64,9 @@ def kernel_source_digest(kernel: str) -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch of the workload's kernel from the committed rocprofv3
-    counter summary, scaled by the plain-copy calibration it holds; None unless the
-    reading was taken on the kernel's current sources."""
+    """HBM bytes per forward (every launch of one forward) of the workload from the
+    committed rocprofv3 counter summary, scaled by the plain-copy calibration it holds;
+    None unless the reading was taken on the kernels' current sources."""
     try:
         with open(COUNTER_FILE) as f:
             rec = json.load(f)
@@ -76,7 +77,7 @@ def measured_traffic(workload: str):
         return None
     if w.get("kernel_digest") != kernel_source_digest(w["kernel"]):
         return None
-    return int(w["hbm_bytes_per_launch"])
+    return int(w["hbm_bytes_per_forward"])
 
 
 def time_forward(plan, bufs, steps: int, warmup: int):
@@ -508,6 +509,9 @@ def main() -> int:
         peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
         bound, achieved, unit = "mfma", flops / kernel_s / 1e12, "TFLOP/s"
     traffic = measured_traffic(wl.name)
+    # the launches of one forward, all inside the HIP-event window that gives kernel_us
+    kernels = {"prefill": "prenorm_kernel + prefill_kernel", "prefill_split": "prefill_kernel (split-K form)",
+               "decode": "decode_kernel", "generic": "generic kernel"}.get(variant, variant)
     out = {
         "metric": METRIC,
         "value": round(wl.tokens * args.steps / wall, 1),
@@ -529,7 +533,8 @@ def main() -> int:
         "mfma_frac": round(flops / kernel_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel_us": round(kernel_s * 1e6, 2), "algorithmic_bytes": nbytes, "flops": flops},
+                     "kernel_us": round(kernel_s * 1e6, 2), "kernels": kernels,
+                     "algorithmic_bytes": nbytes, "flops": flops},
     }
     if cache_s is not None:
         out["kv_cache"] = {"us": round(cache_s * 1e6, 2), "tflops": round(flops / cache_s / 1e12, 2),

@@ -39,8 +39,9 @@
  * buffers alive until the work queued on `stream` has finished.  A plan owns only
  * its device scratch (per-token inverse RMS values, decode partial sums and
  * counters, the split-K prefill form's partial tiles -- up to 67 MB -- and counters,
- * the rotary frequency table), allocated on the device that is current when the plan
- * is created and freed by qkv_plan_destroy.
+ * the prefill pre-pass's bf16 normalise-on-load products -- max_tokens * hidden * 2
+ * bytes -- and the rotary frequency table), allocated on the device that is current
+ * when the plan is created and freed by qkv_plan_destroy.
  *
  * Errors: every call returns a status code; nothing is thrown across the ABI.
  * Arguments are validated before any HIP call is made.
@@ -70,7 +71,9 @@ typedef enum qkv_dtype {
 /* Kernel path a forward of a given token count runs on (see qkv_plan_variant). */
 typedef enum qkv_variant {
   QKV_VARIANT_GENERIC = 0,  /* fp32 FMA tiles: any supported shape, both dtypes        */
-  QKV_VARIANT_PREFILL = 1,  /* bf16 MFMA GEMM, norm-on-load, rotary epilogue           */
+  QKV_VARIANT_PREFILL = 1,  /* two launches: a pre-pass writes bf16(x * w_norm) and
+                               1/rms per row, then the bf16 MFMA GEMM streams them
+                               with the weight and applies 1/rms, bias and rotation     */
   QKV_VARIANT_DECODE = 2,   /* bf16 MFMA weight-streaming kernel for small token counts:
                                up to 192 (or 256) tokens, one launch per 128 tokens     */
   QKV_VARIANT_PREFILL_SPLIT = 3  /* the prefill kernel with the hidden dimension split over

@@ -34,6 +34,7 @@ struct Plan {
   float* kpart;       // split-K prefill: partial tiles
   uint32_t* kcount;   // split-K prefill: per-tile arrival counters
   int kpart_units;    // partial tiles kpart holds
+  void* xw;           // prefill: [max_tokens, H] bf16(x * w_norm) from the pre-pass
   // backward scratch, allocated by the first qkv_backward through the plan
   void* bwd_gy;         // [max_tokens, N] plan dtype
   void* bwd_act;        // [max_tokens, H] plan dtype
@@ -94,6 +95,7 @@ void free_scratch(Plan* pl) {
   if (pl->counters) (void)hipFree(pl->counters);
   if (pl->kpart) (void)hipFree(pl->kpart);
   if (pl->kcount) (void)hipFree(pl->kcount);
+  if (pl->xw) (void)hipFree(pl->xw);
   if (pl->bwd_gy) (void)hipFree(pl->bwd_gy);
   if (pl->bwd_act) (void)hipFree(pl->bwd_act);
   if (pl->bwd_ga) (void)hipFree(pl->bwd_ga);
@@ -104,6 +106,7 @@ void free_scratch(Plan* pl) {
   pl->partials = nullptr;
   pl->counters = nullptr;
   pl->kpart = nullptr;
+  pl->xw = nullptr;
   pl->kcount = nullptr;
   pl->bwd_gy = pl->bwd_act = nullptr;
   pl->bwd_ga = pl->bwd_partial = nullptr;
@@ -207,6 +210,14 @@ qkv_status launch_forward(Plan* pl, int64_t num_tokens, const void* x, const voi
   hipError_t e;
   switch (choose_variant(pl, num_tokens)) {
     case QKV_VARIANT_PREFILL:
+      // pre-pass: bf16(x * w_norm) and 1/rms per row into plan scratch; the MFMA kernel
+      // then streams the activations global -> LDS like the weight
+      e = qkv::launch_prenorm(x, w_norm, pl->xw, pl->inv_rms, a.T, a.H, a.eps, s);
+      if (e != hipSuccess) break;
+      a.x = pl->xw;
+      a.prenormed = true;
+      e = qkv::launch_prefill(a, s);
+      break;
     case QKV_VARIANT_PREFILL_SPLIT:  // the launcher makes the same split choice
       e = qkv::launch_prefill(a, s);
       break;
@@ -282,7 +293,8 @@ qkv_status qkv_plan_create(const qkv_plan_desc* desc, qkv_plan* out_plan) {
     // most CUs idle) and one arrival counter per tile (zeroed once; the kernel leaves
     // them at zero after every forward)
     pl->kpart_units = qkv::prefill_split_units((int)desc->max_tokens, pl->N);
-    ok = hipMalloc(&pl->kpart, sizeof(float) * qkv::prefill_split_floats(pl->kpart_units)) == hipSuccess &&
+    ok = hipMalloc(&pl->xw, (size_t)desc->max_tokens * desc->hidden * 2) == hipSuccess &&
+         hipMalloc(&pl->kpart, sizeof(float) * qkv::prefill_split_floats(pl->kpart_units)) == hipSuccess &&
          hipMalloc(&pl->kcount, sizeof(uint32_t) * qkv::kPrefillSplitMaxTiles) == hipSuccess &&
          hipMemset(pl->kcount, 0, sizeof(uint32_t) * qkv::kPrefillSplitMaxTiles) == hipSuccess &&
          hipDeviceSynchronize() == hipSuccess;
