@@ -417,12 +417,12 @@ def test_variant_names():
                 assert v == "prefill"
 
 
-@pytest.mark.parametrize("cid,T", [(3, 300), (4, 150)])
-def test_graph_replays(cid, T):
-    """A forward captured in a HIP graph (split-K prefill; decode over a 128-token and a
-    22-token chunk): each of several replays, with eager forwards of other inputs in
-    between, writes exactly the eager result; the kernels leave their arrival counters at
-    zero for the next call."""
+@pytest.mark.parametrize("cid,T,variant", [(3, 300, "prefill_split"), (3, 2048, "prefill"), (4, 150, "decode")])
+def test_graph_replays(cid, T, variant):
+    """A forward captured in a HIP graph (split-K prefill; plain prefill, pre-pass then MFMA
+    kernel; decode over a 128-token and a 22-token chunk): each of several replays, with
+    eager forwards of other inputs in between, writes exactly the eager result; the kernels
+    leave their arrival counters at zero for the next call."""
     wl = workloads.WORKLOADS[cid].with_tokens(1, T) if cid == 3 else workloads.WORKLOADS[cid].with_tokens(T, 1)
     inp = workloads.make_inputs(wl, seed=31 + T)
     other = workloads.make_inputs(wl, seed=97 + T)
@@ -430,7 +430,7 @@ def test_graph_replays(cid, T):
                      None if i["bias"] is None else i["bias"].to(DEV), i["pos"].to(DEV))
     args, args2 = dev(inp), dev(other)
     with qkv.Plan.for_workload(wl) as plan:
-        assert plan.variant(T) == ("prefill_split" if cid == 3 else "decode")
+        assert plan.variant(T) == variant
         ref = [t.clone() for t in plan.forward(*args)]
         out = plan.forward(*args)
         stream = torch.cuda.Stream()

@@ -40,7 +40,8 @@
 //     counted at compile time, so prefetches stay in flight across barriers.
 //   * Tiles are numbered so that the ~32 workgroups running at once on one XCD
 //     (workgroups go round-robin over the 8 XCDs) cover 4 row panels x 8 column
-//     panels and share them in that XCD's L2.
+//     panels (2 x 16 for the pre-normalised form on wide projections) and share them
+//     in that XCD's L2.
 //   * Epilogue: y = acc * r[t] + bias; Q and K pairs rotated with cos/sin of
 //     pos * theta^(-2i/d) (turn count reduced in fp64, hardware sin/cos on the
 //     fraction of a turn); bf16 results staged through LDS and stored with 16-byte
@@ -77,7 +78,11 @@ constexpr int kLds = kRowInfo + BM * 12;
 static_assert(kABase + kAStages * kStep <= kLds, "loop rings must fit");
 static_assert(kABase + kAStagesPre * kStep <= kLds, "loop rings must fit");
 static_assert(kLds <= 160 * 1024, "LDS budget of one workgroup");
+// Row panels per tile group: 4, or 2 for the pre-normalised form with at least 48
+// column tiles (measured on the 12288-column shapes: 686 -> 666 us and 1358 -> 1293 us;
+// 2 was slower for the 6144-column GQA shape and for the normalise-on-load gated MLP).
 constexpr int kGroupM = 4;
+constexpr int kGroupMWide = 2;
 
 // LDS byte offset of 16-byte chunk `chunk` (0..3) of row `row` in a [256][32] bf16
 // activation step (64 B rows).  The chunk index is XOR-ed with bits 2..3 of the row,
@@ -161,10 +166,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     const int q8 = G >> 3, r8 = G & 7;
     L = (xcd < r8) ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
   }
-  const int group = L / (kGroupM * tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int idx = L - group * kGroupM * tiles_n;
+  const int group_m = (kPre && tiles_n >= 48) ? kGroupMWide : kGroupM;
+  const int group = L / (group_m * tiles_n);
+  const int first_m = group * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int idx = L - group * group_m * tiles_n;
   const int tm = first_m + idx % gm;
   const int tn = idx / gm;
   const int m0 = tm * BM, n0 = tn * BN;
