@@ -403,6 +403,25 @@ def test_decode_two_full_chunks():
     P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], wl.name)
 
 
+def test_plan_reuse_across_token_counts():
+    """One plan serving forwards of different sizes in turn (plain prefill with its pre-pass
+    scratch, split-K prefill, decode, and plain again): each bit-identical to the same forward
+    through a fresh plan of its own size."""
+    base = workloads.WORKLOADS[3]
+    with qkv.Plan.for_workload(base.with_tokens(1, 2048)) as plan:
+        for T, variant in ((2048, "prefill"), (1537, "prefill"), (300, "prefill_split"), (64, "decode"),
+                           (2048, "prefill")):
+            wl = base.with_tokens(1, T)
+            inp = workloads.make_inputs(wl, seed=T)
+            assert plan.variant(T) == variant
+            got = [t.clone() for t in run(plan, inp)]
+            with qkv.Plan.for_workload(wl) as fresh:
+                assert fresh.variant(T) == variant
+                ref = run(fresh, inp)
+            for name, g, r in zip("QKV", got, ref):
+                assert torch.equal(g, r), f"T={T}: {name} differs from a fresh plan's forward"
+
+
 def test_variant_names():
     for cid in (1, 2, 3, 4, 5):
         wl = workloads.WORKLOADS[cid]
