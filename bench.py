@@ -332,7 +332,8 @@ def unfused_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
                      "rms_norm_hbm_GBps": round(2 * T * H * e / norm / 1e9, 1),
                      "rope_hbm_GBps": round(2 * T * N * e / rope / 1e9, 1),
                      "algorithmic_bytes_fused": fused_bytes, "algorithmic_bytes_unfused": unfused_bytes,
-                     "kernels": "fused: 1 launch; unfused: norm kernel, rocBLAS GEMM, rotation kernel"}
+                     "kernels": "fused: " + ("pre-pass + MFMA kernel" if wl.tokens > 256 else "1 launch")
+                                + "; unfused: norm kernel, rocBLAS GEMM, rotation kernel"}
         del x, w, W, b, pos, q, k, v, xn, y, bufs
         torch.cuda.empty_cache()
     return res
