@@ -321,6 +321,8 @@ def unfused_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
         unfused = _event_time(lambda: plan.forward_unfused(x, w, W, b, pos, out=bufs), steps, warmup)
         norm = _event_time(lambda: plan.rms_norm(x, w, out=xn), steps, warmup)
         rope = _event_time(lambda: plan.rope(y, b, pos), steps, warmup)
+        wn = torch.ones(wl.head_dim, dtype=wl.torch_dtype, device=x.device)
+        norm_rope = _event_time(lambda: plan.head_norm_rope(y, wn, wn, pos), steps, warmup)
         plan.close()
         T, H, N, e = wl.tokens, wl.hidden, wl.n_total, 2
         fused_bytes = wl.algorithmic_bytes()
@@ -328,13 +330,14 @@ def unfused_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
         res[name] = {"tokens": T, "fused_us": round(fused * 1e6, 2), "unfused_us": round(unfused * 1e6, 2),
                      "unfused_over_fused": round(unfused / fused, 3),
                      "rms_norm_us": round(norm * 1e6, 2), "rope_us": round(rope * 1e6, 2),
+                     "head_norm_rope_us": round(norm_rope * 1e6, 2),
                      "gemm_us_by_difference": round((unfused - norm - rope) * 1e6, 2),
                      "rms_norm_hbm_GBps": round(2 * T * H * e / norm / 1e9, 1),
                      "rope_hbm_GBps": round(2 * T * N * e / rope / 1e9, 1),
                      "algorithmic_bytes_fused": fused_bytes, "algorithmic_bytes_unfused": unfused_bytes,
                      "kernels": "fused: " + ("pre-pass + MFMA kernel" if wl.tokens > 256 else "1 launch")
                                 + "; unfused: norm kernel, rocBLAS GEMM, rotation kernel"}
-        del x, w, W, b, pos, q, k, v, xn, y, bufs
+        del x, w, W, b, pos, q, k, v, xn, y, bufs, wn
         torch.cuda.empty_cache()
     return res
 

@@ -173,6 +173,17 @@ qkv_status qkv_rms_norm(qkv_plan plan, int64_t num_tokens, const void* x, const 
 qkv_status qkv_rope(qkv_plan plan, int64_t num_tokens, const void* bias, const int32_t* pos,
                     void* y, void* stream);
 
+/* qkv_head_norm_rope: a norm and the rotation in one pass, in place on y [T, N] laid out
+ * as for qkv_rope.  The Liger-Kernel pages name a fused RMSNorm + RoPE operator without
+ * defining it; in this chain the two are not adjacent, so it is read as the one form in
+ * which they are: every Q head divided by its own RMS over its head_dim values (eps of
+ * the plan) and multiplied by w_qnorm [head_dim], every K head likewise with w_knorm
+ * [head_dim], then each head's rotate-half pairs turned as in qkv_rope; V untouched.
+ * Arithmetic in fp32, one rounding to the plan dtype.  head_dim above 256 returns
+ * QKV_ERR_UNSUPPORTED; otherwise as qkv_rope. */
+qkv_status qkv_head_norm_rope(qkv_plan plan, int64_t num_tokens, const void* w_qnorm,
+                              const void* w_knorm, const int32_t* pos, void* y, void* stream);
+
 /* qkv_forward_unfused: the whole chain as three steps -- qkv_rms_norm into the caller's
  * xn [T, H], the projection y = xn W_qkv as a rocBLAS GEMM (fp32 accumulation, output in
  * the plan dtype) into the caller's y [T, N], then qkv_rope on y.  Q, K and V are the

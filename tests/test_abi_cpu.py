@@ -91,6 +91,7 @@ def test_null_pointers_rejected():
     assert lib.qkv_rms_norm(None, 4, None, None, None, None) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_rope(None, 4, None, None, None, None) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_forward_unfused(None, 4, *([None] * 7), None) == qkv.QKV_ERR_INVALID_ARG
+    assert lib.qkv_head_norm_rope(None, 4, None, None, None, None, None) == qkv.QKV_ERR_INVALID_ARG
     v = ctypes.c_int32()
     assert lib.qkv_plan_variant(None, 4, ctypes.byref(v)) == qkv.QKV_ERR_INVALID_ARG
     assert lib.qkv_plan_destroy(None) == qkv.QKV_OK

@@ -106,3 +106,35 @@ def test_unfused_matches_fused_closely():
         a, b = P.to_f64(a), P.to_f64(b)
         err = np.max(np.abs(a - b) / (1 + np.abs(a)))
         assert err < 2e-2, f"{name}: {err:.3e}"
+
+
+@pytest.mark.parametrize("cid,T,d", [(1, None, None), (4, None, None), (3, 300, None), (5, 129, None),
+                                     (10, 33, 64), (10, 40, 256)])
+def test_head_norm_rope(cid, T, d):
+    """The norm+rotation pass, read as a per-head RMSNorm of every Q and K head followed by
+    the rotation: the oracle's rms_norm over each head's values, then its rope."""
+    if cid == 10:
+        wl = workloads.Workload(10, f"hnr_d{d}", 1, T, 1024, 4, 2, d, False, 1e4, 1e-6, "bf16", "per_seq")
+    else:
+        wl = workloads.WORKLOADS[cid]
+        if T is not None:
+            wl = wl.with_tokens(1, T)
+    d = wl.head_dim
+    inp = workloads.make_inputs(wl, seed=51 + cid)
+    g = torch.Generator().manual_seed(509 + cid)
+    y0 = torch.randn(wl.tokens, wl.n_total, generator=g).to(wl.torch_dtype)
+    wq = (1 + 0.1 * torch.randn(d, generator=g)).to(wl.torch_dtype)
+    wk = (1 + 0.1 * torch.randn(d, generator=g)).to(wl.torch_dtype)
+    with qkv.Plan.for_workload(wl) as plan:
+        got = P.to_f64(plan.head_norm_rope(y0.to(DEV), wq.to(DEV), wk.to(DEV), inp["pos"].to(DEV)))
+    y, pos, T = P.to_f64(y0), P.to_f64(inp["pos"]), wl.tokens
+    nq, nkv = wl.n_q, wl.n_kv
+
+    def norm_rotate(block, w):
+        heads = qkv_oracle.rms_norm(block.reshape(-1, d), P.to_f64(w), wl.eps).reshape(T, -1)
+        return qkv_oracle.rope(heads, pos, d, wl.rope_theta)
+
+    ref = np.concatenate([norm_rotate(y[:, :nq], wq), norm_rotate(y[:, nq:nq + nkv], wk), y[:, nq + nkv:]], axis=1)
+    bound = REL[wl.dtype] * np.abs(ref) + 1e-5 * (1 + np.abs(ref).max(axis=1, keepdims=True))
+    excess = np.abs(got - ref) - bound
+    assert excess.max() <= 0, f"{wl.name}: worst excess {excess.max():.3e} at {np.unravel_index(excess.argmax(), excess.shape)}"

@@ -35,6 +35,7 @@ EXPORTS = {
     "qkv_rms_norm": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp]),
     "qkv_rope": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp]),
     "qkv_forward_unfused": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "qkv_head_norm_rope": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp]),
     "qkv_plan_variant": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)]),
     "qkv_plan_destroy": (ctypes.c_int, [_vp]),
     "qkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -306,6 +307,20 @@ class Plan:
         self._check_tensor(pos, "pos", (T,), torch.int32)
         _check(self._lib.qkv_rope(self.handle, T, _ptr(bias), _ptr(pos), _ptr(y), _stream_handle(stream)),
                "qkv_rope")
+        return y
+
+    def head_norm_rope(self, y: torch.Tensor, w_qnorm: torch.Tensor, w_knorm: torch.Tensor, pos: torch.Tensor,
+                       stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """Per-head RMSNorm of the Q and K heads of y [T, N], then their rotation, in place
+        (qkv_head_norm_rope)."""
+        T = y.shape[0]
+        N = self.n_q + 2 * self.n_kv
+        self._check_tensor(y, "y", (T, N), self.dtype)
+        self._check_tensor(w_qnorm, "w_qnorm", (self.head_dim,), self.dtype)
+        self._check_tensor(w_knorm, "w_knorm", (self.head_dim,), self.dtype)
+        self._check_tensor(pos, "pos", (T,), torch.int32)
+        _check(self._lib.qkv_head_norm_rope(self.handle, T, _ptr(w_qnorm), _ptr(w_knorm), _ptr(pos), _ptr(y),
+                                            _stream_handle(stream)), "qkv_head_norm_rope")
         return y
 
     def forward_unfused(self, x: torch.Tensor, w_norm: torch.Tensor, w_qkv: torch.Tensor,

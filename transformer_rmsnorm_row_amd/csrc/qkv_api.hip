@@ -398,6 +398,24 @@ qkv_status qkv_rope(qkv_plan plan, int64_t num_tokens, const void* bias, const i
   return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
 }
 
+qkv_status qkv_head_norm_rope(qkv_plan plan, int64_t num_tokens, const void* w_qnorm, const void* w_knorm,
+                              const int32_t* pos, void* y, void* stream) {
+  Plan* pl = as_plan(plan);
+  if (!pl) return QKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return QKV_OK;
+  if (num_tokens < 0 || num_tokens > pl->desc.max_tokens) return QKV_ERR_INVALID_ARG;
+  if (!w_qnorm || !w_knorm || !pos || !y || !aligned(w_qnorm, 16) || !aligned(w_knorm, 16) || !aligned(pos, 4) ||
+      !aligned(y, 16))
+    return QKV_ERR_INVALID_ARG;
+  if (pl->desc.head_dim > 256) return QKV_ERR_UNSUPPORTED;
+  qkv_status st = check_device(pl);
+  if (st != QKV_OK) return st;
+  const hipError_t e =
+      qkv::launch_head_norm_rope(y, w_qnorm, w_knorm, pos, pl->rev_freq, (int)num_tokens, pl->N, pl->Nq, pl->Nkv,
+                                 pl->desc.head_dim, (float)pl->desc.eps, pl->bf16, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
+}
+
 qkv_status qkv_forward_unfused(qkv_plan plan, int64_t num_tokens, const void* x, const void* w_norm,
                                const void* w_qkv, const void* bias, const int32_t* pos, void* xn, void* y,
                                void* stream) {

@@ -16,4 +16,11 @@ hipError_t launch_rms_norm(const void* x, const void* w_norm, void* xn, int T, i
 hipError_t launch_rope(void* y, const void* bias, const int32_t* pos, const double* rev_freq, int T, int N, int Nq,
                        int Nkv, int d, bool bf16, hipStream_t stream);
 
+// In place on y [T, N]: every Q head (weight wq [d]) and K head (weight wk [d]) divided
+// by its own RMS over d (eps), multiplied by the weight, then turned like launch_rope;
+// V untouched (d % 8 == 0, d <= 256).
+hipError_t launch_head_norm_rope(void* y, const void* wq, const void* wk, const int32_t* pos,
+                                 const double* rev_freq, int T, int N, int Nq, int Nkv, int d, float eps, bool bf16,
+                                 hipStream_t stream);
+
 }  // namespace qkv

@@ -15,6 +15,14 @@
 //                    column (when given) and turns each rotate-half pair (i, i + d/2) of the
 //                    Q and K heads by pos[t] * theta^(-2i/d); V columns only get the bias.
 //                    Each thread takes 4 consecutive pairs of one head.
+//   head_norm_rope_kernel  the norm and the rotation in one pass, read as a per-head
+//                    RMSNorm of every Q and K head of y (weights [d] for Q and for K,
+//                    eps of the plan) followed by the turn of its pairs: one wavefront per
+//                    (token, head) item at a time, about 8 items per wavefront in a grid
+//                    stride, lane j holding the pair (j, j + d/2) (j + 64 for larger heads),
+//                    the head's sum of squares reduced across the wave.
+#include <algorithm>
+
 #include "device_common.h"
 #include "unfused.h"
 
@@ -140,7 +148,81 @@ __global__ __launch_bounds__(256) void rope_kernel(void* __restrict__ y, const v
   }
 }
 
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* p, size_t i) {
+  if constexpr (BF16)
+    return bf16_lo((uint32_t)((const uint16_t*)p)[i]);
+  else
+    return ((const float*)p)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store1(void* p, size_t i, float v) {
+  if constexpr (BF16)
+    ((uint16_t*)p)[i] = f32_to_bf16(v);
+  else
+    ((float*)p)[i] = v;
+}
+
+// Pairs per lane: up to 2 (head_dim <= 256).
+template <bool BF16>
+__global__ __launch_bounds__(256) void head_norm_rope_kernel(void* __restrict__ y, const void* __restrict__ wq,
+                                                             const void* __restrict__ wk,
+                                                             const int32_t* __restrict__ pos,
+                                                             const double* __restrict__ rev_freq, int T, int N,
+                                                             int nq_heads, int rot_heads, int d, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int half = d / 2;
+  const int items = T * rot_heads, stride = gridDim.x * 4;
+  // each wavefront walks (token, rotated head) items with a grid stride
+  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < items; item += stride) {
+    const int row = item / rot_heads, head = item % rot_heads;
+    const void* w = head < nq_heads ? wq : wk;
+    const size_t base = (size_t)row * N + (size_t)head * d;
+    float u[2] = {0.f, 0.f}, v[2] = {0.f, 0.f}, ss = 0.f;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = lane + 64 * r;
+      if (i < half) {
+        u[r] = load1<BF16>(y, base + i);
+        v[r] = load1<BF16>(y, base + i + half);
+        ss = fmaf(u[r], u[r], fmaf(v[r], v[r], ss));
+      }
+    }
+    const float rinv = rsqrtf(wave_sum(ss) / (float)d + eps);
+    const int32_t p = pos[row];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = lane + 64 * r;
+      if (i < half) {
+        const float a = u[r] * rinv * load1<BF16>(w, i), b = v[r] * rinv * load1<BF16>(w, i + half);
+        float cs, sn;
+        rope_cos_sin(p, rev_freq[i], cs, sn);
+        store1<BF16>(y, base + i, a * cs - b * sn);
+        store1<BF16>(y, base + i + half, b * cs + a * sn);
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_head_norm_rope(void* y, const void* wq, const void* wk, const int32_t* pos,
+                                 const double* rev_freq, int T, int N, int Nq, int Nkv, int d, float eps, bool bf16,
+                                 hipStream_t stream) {
+  const int nq_heads = Nq / d, rot_heads = (Nq + Nkv) / d;
+  const int items = T * rot_heads;
+  // about 8 items per wavefront, at least 4096 workgroups when there is that much work
+  const int blocks = std::max(1, std::min((items + 3) / 4, std::max(4096, (items + 31) / 32)));
+  dim3 grid((unsigned)blocks), block(256);
+  if (bf16)
+    head_norm_rope_kernel<true><<<grid, block, 0, stream>>>(y, wq, wk, pos, rev_freq, T, N, nq_heads, rot_heads, d,
+                                                            eps);
+  else
+    head_norm_rope_kernel<false><<<grid, block, 0, stream>>>(y, wq, wk, pos, rev_freq, T, N, nq_heads, rot_heads,
+                                                             d, eps);
+  return hipGetLastError();
+}
 
 hipError_t launch_rms_norm(const void* x, const void* w_norm, void* xn, int T, int H, float eps, bool bf16,
                            hipStream_t stream) {
