@@ -34,8 +34,9 @@ struct ForwardArgs {
   int T, H, N, Nq, Nkv, d;
   float eps;
   bool bf16;
-  // x holds bf16(x * w_norm) and inv_rms each row's 1/rms, written by launch_prenorm:
-  // the plain prefill kernel then loads activations like the weight, with no conversion
+  // x holds bf16(x * w_norm) pre-tiled and inv_rms each row's 1/rms, written by
+  // launch_prenorm: the plain prefill kernel then loads activations like the weight, with
+  // no conversion
   bool prenormed;
 };
 
@@ -67,7 +68,9 @@ hipError_t launch_backward_pre_gemm(const BackwardArgs& b, hipStream_t stream);
 // dx and the norm-weight gradient, once ga = gy W^T is in b.ga
 hipError_t launch_backward_post_gemm(const BackwardArgs& b, hipStream_t stream);
 
-// One pass over bf16 x [T, H]: xw = bf16(x * w_norm) and inv_rms[t] = 1/rms of row t.
+// One pass over bf16 x [T, H]: xw = bf16(x * w_norm), tiled per 256-row panel and 32-wide
+// k step in the prefill kernel's LDS order (T rounded up to 256 rows, the extra rows zero),
+// and inv_rms[t] = 1/rms of row t.
 hipError_t launch_prenorm(const void* x, const void* w_norm, void* xw, float* inv_rms, int T, int H, float eps,
                           hipStream_t stream);
 hipError_t launch_inv_rms(const void* x, float* inv_rms, int T, int H, float eps, bool bf16,

@@ -31,9 +31,11 @@
 //     epilogue, which is the same product (diag(r) X diag(w) W = diag(r) (X diag(w)) W).
 //   * Pre-normalised form (kPre), the one plain prefill forwards use: a one-pass
 //     pre-kernel writes bf16(x * w_norm) and each row's 1/rms (the same products and
-//     rounding), and this kernel then streams the activation steps global -> LDS by DMA
-//     exactly like the weight (4-deep ring, 3 steps ahead), with no register staging
-//     and no conversion in the loop; 1/rms comes from the pre-pass.  The pre-pass costs
+//     rounding), laid out per 256-row panel and 32-wide step exactly as the LDS holds a
+//     step, and this kernel then streams the activation steps global -> LDS by DMA like
+//     the weight (4-deep ring, 3 steps ahead, 1 KB of consecutive bytes per
+//     instruction), with no register staging and no conversion in the loop; 1/rms
+//     comes from the pre-pass.  The pre-pass costs
 //     one read and one write of x, and saves more than that: 48 column tiles no longer
 //     each redo the conversion of the same rows.
 //   * All vector-memory instructions of the loop are inline assembly with waits
@@ -214,22 +216,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     }
     b_voff[i] = ((kofs + 4u * wave + krow) * N + col) * 2u;
   }
-  // ---- pre-normalised activation DMA (kPre): wave w fills rows 32w + 16i .. +15 of
-  // each step, i = 0, 1; each instruction is one 1 KB run of LDS = 16 rows of 64 B,
-  // lane l filling physical chunk l % 4 of row 32w + 16i + l / 4, i.e. logical chunk
-  // (l % 4) ^ ((row / 4) % 4) = (l % 4) ^ ((l / 16) % 4) of a_off's swizzle.
+  // ---- pre-normalised activation DMA (kPre): the pre-pass stored each 256-row panel's
+  // 32-wide k steps as [256 rows][64 B] images already in a_off's swizzled order, so wave
+  // w's instruction i copies the 1 KB of rows 32w + 16i .. +15 of a step as it lies.
   uint32_t xa_voff[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t r = 32u * wave + 16u * i + (lane >> 2);
-    const uint32_t c = (lane & 3u) ^ ((lane >> 4) & 3u);
-    xa_voff[i] = ((uint32_t)(m0 + r) * H + kofs + 8u * c) * 2u;
-  }
+  for (int i = 0; i < 2; ++i)
+    xa_voff[i] = (uint32_t)tm * (uint32_t)H * 512u + (32u * wave + 16u * i) * 64u + (uint32_t)lane * 16u;
   const uint64_t wbase = reinterpret_cast<uint64_t>(a.w);
   const u32x4 w_rsrc = {(uint32_t)wbase, (uint32_t)(wbase >> 32), (uint32_t)H * (uint32_t)N * 2u,
                         (uint32_t)kBufferWord3};
   const uint64_t xbase = reinterpret_cast<uint64_t>(a.x), nbase = reinterpret_cast<uint64_t>(a.w_norm);
   const u32x4 x_rsrc = {(uint32_t)xbase, (uint32_t)(xbase >> 32), (uint32_t)T * (uint32_t)H * 2u, (uint32_t)kBufferWord3};
+  // the pre-tiled activations span whole 256-row panels
+  const u32x4 xa_rsrc = {(uint32_t)xbase, (uint32_t)(xbase >> 32), (uint32_t)tiles_m * (uint32_t)H * 512u,
+                         (uint32_t)kBufferWord3};
   const u32x4 n_rsrc = {(uint32_t)nbase, (uint32_t)(nbase >> 32), (uint32_t)H * 2u, (uint32_t)kBufferWord3};
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
@@ -289,8 +290,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + kABase + astage * kStep + (32 * wave + 16 * i) * 64);
-      const uint32_t voff = xa_voff[i] + k0 * 2u;
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(voff), "s"(x_rsrc)
+      const uint32_t voff = xa_voff[i] + k0 * 512u;  // step t's image starts t * 16 KB into the panel
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(voff), "s"(xa_rsrc)
                    : "m0");
     }
   };

@@ -34,7 +34,7 @@ struct Plan {
   float* kpart;       // split-K prefill: partial tiles
   uint32_t* kcount;   // split-K prefill: per-tile arrival counters
   int kpart_units;    // partial tiles kpart holds
-  void* xw;           // prefill: [max_tokens, H] bf16(x * w_norm) from the pre-pass
+  void* xw;           // prefill: bf16(x * w_norm) from the pre-pass, max_tokens rounded up to 256 rows
   // backward scratch, allocated by the first qkv_backward through the plan
   void* bwd_gy;         // [max_tokens, N] plan dtype
   void* bwd_act;        // [max_tokens, H] plan dtype
@@ -293,7 +293,7 @@ qkv_status qkv_plan_create(const qkv_plan_desc* desc, qkv_plan* out_plan) {
     // most CUs idle) and one arrival counter per tile (zeroed once; the kernel leaves
     // them at zero after every forward)
     pl->kpart_units = qkv::prefill_split_units((int)desc->max_tokens, pl->N);
-    ok = hipMalloc(&pl->xw, (size_t)desc->max_tokens * desc->hidden * 2) == hipSuccess &&
+    ok = hipMalloc(&pl->xw, (size_t)(desc->max_tokens + 255) / 256 * 256 * desc->hidden * 2) == hipSuccess &&
          hipMalloc(&pl->kpart, sizeof(float) * qkv::prefill_split_floats(pl->kpart_units)) == hipSuccess &&
          hipMalloc(&pl->kcount, sizeof(uint32_t) * qkv::kPrefillSplitMaxTiles) == hipSuccess &&
          hipMemset(pl->kcount, 0, sizeof(uint32_t) * qkv::kPrefillSplitMaxTiles) == hipSuccess &&

@@ -45,39 +45,49 @@ __global__ __launch_bounds__(256) void inv_rms_kernel(const void* __restrict__ x
 }
 
 // Pre-pass of the prefill kernel's pre-normalised form: the same row reduction, and
-// the normalise-on-load product bf16(x * w_norm) written out so the GEMM can stream it
-// global -> LDS like the weight.  One wavefront per row, 16-byte loads and stores.
+// the normalise-on-load product bf16(x * w_norm) written out pre-tiled in the order the
+// kernel's LDS holds it, so that each of its activation DMA instructions reads 1 KB of
+// consecutive bytes.  Tiled layout: [T_pad / 256 panels][H / 32 steps][256 rows][4 x 16 B],
+// 16-byte chunk q (k = 8q .. 8q + 7 of the step) of row r stored at chunk q ^ ((r / 4) % 4).
+// One wavefront per row (rows T .. T_pad - 1 of the last panel are written as zeros),
+// 16-byte loads and stores.
 __global__ __launch_bounds__(256) void prenorm_kernel(const void* __restrict__ x, const void* __restrict__ w,
-                                                      void* __restrict__ xw, float* __restrict__ out, int T, int H,
-                                                      float eps) {
+                                                      void* __restrict__ xw, float* __restrict__ out, int T,
+                                                      int T_pad, int H, float eps) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= T) return;
+  if (row >= T_pad) return;
   const uint32_t row_bytes = (uint32_t)H * 2u;  // multiple of 16 (H % 8 == 0)
   const char* base = (const char*)x + (size_t)row * row_bytes;
-  char* dst = (char*)xw + (size_t)row * row_bytes;
+  const uint32_t r = (uint32_t)row & 255u, swz = (r >> 2) & 3u;
+  char* panel = (char*)xw + (size_t)(row >> 8) * 256u * row_bytes;
   float ss0 = 0.f, ss1 = 0.f;
 #pragma unroll 4
   for (uint32_t off = (uint32_t)lane * 16u; off < row_bytes; off += 64u * 16u) {
-    const u32x4 v = __builtin_nontemporal_load((const u32x4*)(base + off));
-    const u32x4 g = *(const u32x4*)((const char*)w + off);
-    u32x4 o;
+    const uint32_t c = off >> 4, step = c >> 2, q = c & 3u;
+    u32x4 o = {0u, 0u, 0u, 0u};
+    if (row < T) {
+      const u32x4 v = __builtin_nontemporal_load((const u32x4*)(base + off));
+      const u32x4 g = *(const u32x4*)((const char*)w + off);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float lo = bf16_lo(v[c]), hi = bf16_hi(v[c]);
-      ss0 = fmaf(lo, lo, ss0);
-      ss1 = fmaf(hi, hi, ss1);
-      o[c] = pack_bf16x2(lo * bf16_lo(g[c]), hi * bf16_hi(g[c]));
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo(v[e]), hi = bf16_hi(v[e]);
+        ss0 = fmaf(lo, lo, ss0);
+        ss1 = fmaf(hi, hi, ss1);
+        o[e] = pack_bf16x2(lo * bf16_lo(g[e]), hi * bf16_hi(g[e]));
+      }
     }
-    *(u32x4*)(dst + off) = o;
+    *(u32x4*)(panel + ((size_t)step * 256u + r) * 64u + ((q ^ swz) << 4)) = o;
   }
+  if (row >= T) return;
   const float ss = wave_sum(ss0 + ss1);
   if (lane == 0) out[row] = rsqrtf(ss / (float)H + eps);
 }
 
 hipError_t launch_prenorm(const void* x, const void* w_norm, void* xw, float* inv_rms, int T, int H, float eps,
                           hipStream_t stream) {
-  prenorm_kernel<<<dim3((T + 3) / 4), dim3(256), 0, stream>>>(x, w_norm, xw, inv_rms, T, H, eps);
+  const int T_pad = (T + 255) / 256 * 256;
+  prenorm_kernel<<<dim3((T_pad + 3) / 4), dim3(256), 0, stream>>>(x, w_norm, xw, inv_rms, T, T_pad, H, eps);
   return hipGetLastError();
 }
 
