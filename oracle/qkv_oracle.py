@@ -195,9 +195,11 @@ def qkv_backward(x, w_norm, w_qkv, pos, gq, gk, gv, num_q_heads: int, num_kv_hea
         dx[t,j] = r w_j ga_j - (r^3 / H) x_j sum_k ga_k w_k x_k.
 
     Returns (dx, dw_norm, dw_qkv, dbias or None), float64.  With return_scales, also
-    the root-sum-square of the terms that each element of those gradients sums (over
-    tokens for dw_norm, dW and db; over output columns for dx), the scale that a sum
-    of individually rounded terms is accurate to.
+    the root-sum-square of the terms that each element of those gradients sums, the
+    scale that a sum of individually rounded terms is accurate to: over tokens for
+    dw_norm (terms ga x r), dW (terms a gy) and db (terms gy); for dx, which is two
+    separate sums, the root-sum-square of the first's terms r w_j gy_n W[j,n] (over
+    output columns n) plus that of the second's terms (r^3/H) x_j ga_k w_k x_k (over k).
     """
     x = np.asarray(x, dtype=np.float64)
     w = np.asarray(w_norm, dtype=np.float64)

@@ -461,4 +461,71 @@ def pin_backward_scale_invariance(o):
     _close(dots, np.zeros(T), 1e-12, "x . dx")
 
 
+def pin_backward_scales_root_sum_square(o):
+    """The tolerance scales of the backward (return_scales) against the root-sum-square
+    of every gradient element's terms, each term enumerated one at a time with plain
+    loops on a tiny case with a bias.  The terms come from the chain rule (rotation
+    transposed, projection, norm); their sums must equal the oracle's gradients, which
+    the finite-difference pin fixes independently, so the terms are the right ones
+    before their squares are summed.  For dx the two sums (the weighted projection
+    gradient, and the norm's inner product times its factor) are separate, and the
+    scale is the sum of their two root-sum-squares."""
+    rng = _rng(63)
+    T, H, nq, nkv, d, eps, theta = 3, 8, 2, 1, 4, 1e-3, 100.0
+    half = d // 2
+    N = (nq + 2 * nkv) * d
+    x = rng.standard_normal((T, H)) * np.array([[0.3], [1.0], [4.0]])
+    w = 1.0 + 0.2 * rng.standard_normal(H)
+    W = 0.5 * rng.standard_normal((H, N))
+    pos = [0, 7, 19]
+    gq = rng.standard_normal((T, nq * d))
+    gk = rng.standard_normal((T, nkv * d))
+    gv = rng.standard_normal((T, nkv * d))
+    (dx, dw, dW, db), (s_dx, s_dw, s_dW, s_db) = o.qkv_backward(
+        x, w, W, np.array(pos), gq, gk, gv, nq, nkv, d, eps, theta, with_bias=True, return_scales=True)
+
+    # upstream gradient of the projection output: each Q/K pair (i, i + d/2) turned
+    # back by its angle (the transpose of the forward rotation), V as it arrives
+    g_up = np.concatenate([gq, gk, gv], axis=1)
+    gy = [[0.0] * N for _ in range(T)]
+    for t in range(T):
+        for n in range(N):
+            head_start = (n // d) * d
+            i = (n - head_start) % half
+            if n >= (nq + nkv) * d:
+                gy[t][n] = float(g_up[t, n])
+                continue
+            ang = pos[t] * theta ** (-2.0 * i / d)
+            u, v = g_up[t, head_start + i], g_up[t, head_start + i + half]
+            if n - head_start < half:
+                gy[t][n] = u * math.cos(ang) + v * math.sin(ang)
+            else:
+                gy[t][n] = v * math.cos(ang) - u * math.sin(ang)
+    r = [1.0 / math.sqrt(sum(x[t, k] ** 2 for k in range(H)) / H + eps) for t in range(T)]
+    act = [[x[t, k] * r[t] * w[k] for k in range(H)] for t in range(T)]
+    ga = [[sum(gy[t][n] * W[k, n] for n in range(N)) for k in range(H)] for t in range(T)]
+
+    def rss(terms):
+        return math.sqrt(sum(v * v for v in terms))
+
+    for n in range(N):
+        terms = [gy[t][n] for t in range(T)]
+        _close(sum(terms), db[n], 1e-12, "db terms")
+        _close(rss(terms), s_db[n], 1e-12, "db scale")
+    for k in range(H):
+        for n in range(N):
+            terms = [act[t][k] * gy[t][n] for t in range(T)]
+            _close(sum(terms), dW[k, n], 1e-12, "dW terms")
+            _close(rss(terms), s_dW[k, n], 1e-12, "dW scale")
+        terms = [ga[t][k] * x[t, k] * r[t] for t in range(T)]
+        _close(sum(terms), dw[k], 1e-12, "dw_norm terms")
+        _close(rss(terms), s_dw[k], 1e-12, "dw_norm scale")
+    for t in range(T):
+        for j in range(H):
+            first = [r[t] * w[j] * gy[t][n] * W[j, n] for n in range(N)]
+            second = [-(r[t] ** 3 / H) * x[t, j] * ga[t][k] * w[k] * x[t, k] for k in range(H)]
+            _close(sum(first) + sum(second), dx[t, j], 1e-12, "dx terms")
+            _close(rss(first) + rss(second), s_dx[t, j], 1e-12, "dx scale")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -52,6 +52,13 @@ MUTANTS = {
     "bwd_dw_without_r": [("dw = np.sum(ga * x * r[:, None], axis=0)", "dw = np.sum(ga * x, axis=0)")],
     "bwd_dW_from_rotated_grads": [("dW = a.T @ gy", "dW = a.T @ np.concatenate([np.asarray(gq), np.asarray(gk), "
                                                     "np.asarray(gv)], axis=1)")],
+    "bwd_scale_no_sqrt": [("sq = lambda m: np.sqrt(np.maximum(m, 0.0))", "sq = lambda m: np.maximum(m, 0.0)")],
+    "bwd_scale_abs_sum_for_dW": [("sq((a * a).T @ (gy * gy))", "np.abs(a).T @ np.abs(gy)")],
+    "bwd_scale_dx_norm_part_dropped": [
+        ("\n                  + (r ** 3 / H)[:, None] * np.abs(x) * sq(np.sum((ga * w[None, :] * x) ** 2, axis=1))[:, None],",
+         ",")],
+    "bwd_scale_dw_without_r": [("sq(np.sum((ga * x * r[:, None]) ** 2, axis=0))", "sq(np.sum((ga * x) ** 2, axis=0))")],
+    "bwd_scale_db_plain_sum": [("sq(np.sum(gy * gy, axis=0))", "np.abs(np.sum(gy, axis=0))")],
     "k_v_swapped": [("k = rope(y[:, n_q:n_q + n_kv], pos, head_dim, theta)",
                      "k = rope(y[:, n_q + n_kv:], pos, head_dim, theta)"),
                     ("v = y[:, n_q + n_kv:].copy()", "v = y[:, n_q:n_q + n_kv].copy()")],

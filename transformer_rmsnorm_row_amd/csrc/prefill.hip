@@ -361,9 +361,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // A bare s_barrier: this wave's LDS reads and loads may still be in flight.
+  // End of a memory phase: this wave's fragment reads have returned (the other group
+  // issues DMA into the ring slot it read one step earlier right after this barrier),
+  // while its global loads and DMA stay in flight.
   auto raw_barrier = [&]() {
     __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -374,14 +377,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   // slot t % 4), issue x(t + 2) into register set t % 2 and W(t + 3) into weight slot
   // (t + 3) % 4, and wait until this wave's part of W(t + 1) has landed.  Per wave the
   // vector-memory order is ..., W(t + 1), x(t + 1), W(t + 2), x(t + 2), W(t + 3), so
-  // that wait is vmcnt(10).  The phase ends at a bare barrier: its fragment reads may
-  // still be in flight, since nothing written in the next phase (the other group's
-  // weight DMA into slot (t - 1) % 4, this group's conversion into activation slot
-  // (t + 1) % 2) aliases them.  Compute phase: wait for x(t + 1) (vmcnt(7)), the MFMAs
+  // that wait is vmcnt(10).  The phase ends at a barrier that waits for this wave's
+  // fragment reads but not for its loads: in the next phase the other group issues its
+  // part of W(t + 3) into slot (t - 1) % 4, which this wave read in its previous memory
+  // phase, and the DMA must not land before those reads have returned.  Compute phase:
+  // wait for x(t + 1) (vmcnt(7)), the MFMAs
   // of step t and the conversion of x(t + 1) into activation slot (t + 1) % 2, closed
   // by a full barrier so the converted rows are in LDS before this group reads them.
   // Slot reuse is safe: weight slot (t + 3) % 4 held step t - 1, which both groups
-  // read in memory phases that ended before this phase began; activation slot
+  // read in memory phases that ended, reads returned, before this phase began; activation slot
   // (t + 1) % 2 held step t - 1 of this group's rows, read in its previous memory
   // phase; register set t % 2 was converted in the previous compute phase.  Every wave
   // has its part of W(t + 1) complete before the barrier that ends its memory phase t,
