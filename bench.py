@@ -5,27 +5,35 @@
 
 One step is one forward of the whole chain (row reduction, normalise-on-load
 projection, bias, rotary embedding, single store of Q/K/V) over one batch of
-seeded synthetic input already resident in HBM.  W untimed steps, then exactly K
-steps between two device synchronisations.  Prints one JSON line.
+seeded synthetic input already resident in HBM: for the prefill workloads one launch
+of the 128 x 512 MFMA kernel, whose normalised activations never leave the chip.  W
+untimed steps, then exactly K steps between two device synchronisations.  Prints one
+JSON line.
 
-Besides the headline workload (Llama-7B-shaped prefill, 4 x 2048 tokens) the
-line carries:
-  roofline      the dominant kernel's achieved rate against the MI355X peak of its
-                bound (bf16 dense MFMA 2516.6 TFLOP/s for prefill, HBM 8 TB/s for
-                decode), from HIP events on the stream the kernels run on, plus the
-                HBM traffic measured by rocprofv3 counters when it is current;
+The headline workload is the largest configuration, the Qwen-7B-shaped prefill with
+QKV bias (2 x 8192 tokens).  Besides it the line carries:
+  roofline      the forward's achieved rate against the MI355X peak of its bound
+                (bf16 dense MFMA 2516.6 TFLOP/s for prefill, HBM 8 TB/s for decode), from
+                HIP events on the stream the kernel runs on, plus the HBM traffic measured
+                by rocprofv3 counters when it is current;
+  configs       every configuration at full size: GPU time and rate, the fp64 oracle's
+                full forward timed on the host cores, the worst parity ratio against it
+                over every element of Q, K and V (with where it occurs), and SHA-256
+                digests of the seeded inputs;
+  prefill_prepass_opt_in  the same forward with the opt-in pre-pass form (two launches,
+                normalised activations written to HBM and read back), timed beside it;
   decode        the 64-token decode step streaming its weight from HBM (8 weight
                 copies rotated so the 256 MB last-level cache cannot hold them);
-  other_workloads  every other forward workload (tiny fp32, Llama-3-8B GQA prefill,
-                the decode step warm, Qwen-7B prefill with bias) at full size, and
-                two mid-size batches (512 tokens on the GQA shape, 128 decode tokens);
+  other_workloads  two mid-size batches (512 tokens on the GQA shape, 128 decode tokens);
   unfused       the chain as three steps (RMSNorm kernel, rocBLAS GEMM, bias+RoPE
                 kernel) against the fused forward, on the prefill and decode shapes;
+  kv_cache, swiglu, backward  the built next steps (K/V into a cache, the gated MLP,
+                the backward on the Llama-7B shape);
   prefill_zero_weight  the headline forward with an all-zero weight, a labelled
                 diagnostic: how much of the prefill time is the clock lost to the
                 matrix cores' power draw on random operands;
   cpu_baseline  the fp64 CPU oracle on the host cores, one full forward of the
-                same workload (a reported baseline, not a target).
+                headline workload (a reported baseline, not a target).
 """
 from __future__ import annotations
 
@@ -47,8 +55,10 @@ COUNTER_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
 
 # sources each kernel is built from: a counter reading stays valid while these are unchanged
-# (the plain prefill forward is the pre-pass of rownorm.hip, then prefill_kernel)
+# (a plain prefill forward is one launch of prefill_wide_kernel; the opt-in pre-pass form
+# is the pre-pass of rownorm.hip, then prefill_kernel)
 KERNEL_SOURCES = {
+    "prefill_wide_kernel": ("prefill_wide.hip", "device_common.h", "launch.h"),
     "prefill_kernel": ("prefill.hip", "rownorm.hip", "device_common.h", "launch.h"),
     "decode_kernel": ("decode.hip", "device_common.h", "launch.h"),
 }
@@ -335,8 +345,7 @@ def unfused_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
                      "rms_norm_hbm_GBps": round(2 * T * H * e / norm / 1e9, 1),
                      "rope_hbm_GBps": round(2 * T * N * e / rope / 1e9, 1),
                      "algorithmic_bytes_fused": fused_bytes, "algorithmic_bytes_unfused": unfused_bytes,
-                     "kernels": "fused: " + ("pre-pass + MFMA kernel" if wl.tokens > 256 else "1 launch")
-                                + "; unfused: norm kernel, rocBLAS GEMM, rotation kernel"}
+                     "kernels": "fused: 1 launch; unfused: norm kernel, rocBLAS GEMM, rotation kernel"}
         del x, w, W, b, pos, q, k, v, xn, y, bufs, wn
         torch.cuda.empty_cache()
     return res
@@ -368,41 +377,128 @@ def swiglu_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
             "algorithmic_bytes": wl.algorithmic_bytes()}
 
 
-def other_workloads_leg(qkv, workloads, skip: str, steps: int = 30, warmup: int = 5):
-    """Every other forward workload at its full size, back-to-back calls timed with HIP
-    events on the current stream: prefill ones against the bf16 (or fp32) matrix peak,
-    the decode step against HBM (warm last-level cache here; the decode leg streams it
-    cold)."""
+def _worst_ratio(gpu, ref):
+    """max |gpu - ref| / (1 + |ref|) over one output tensor, with its (t, column);
+    a non-finite GPU value counts as infinite."""
+    import numpy as np
+    ratio = np.abs(gpu - ref) / (1.0 + np.abs(ref))
+    ratio = np.where(np.isfinite(gpu), ratio, np.inf)
+    t, c = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    return float(ratio[t, c]), int(t), int(c)
+
+
+def _oracle_threads() -> int:
+    try:
+        import threadpoolctl
+        return int(max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1))
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def _oracle_forward(wl, inp):
+    """One full forward of the fp64 oracle on the host cores: (Q, K, V), seconds."""
+    import numpy as np
+    import torch
+    from oracle import qkv_oracle
+    to64 = lambda t: None if t is None else t.to(dtype=torch.float64).numpy()
+    args = (to64(inp["x"]), to64(inp["w_norm"]), to64(inp["w_qkv"]), to64(inp["bias"]),
+            inp["pos"].numpy().astype(np.int64), wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.eps,
+            wl.rope_theta)
+    t0 = time.perf_counter()
+    out = qkv_oracle.qkv_forward(*args)
+    return out, time.perf_counter() - t0
+
+
+def configs_leg(qkv, workloads, steps: int = 30, warmup: int = 5, headline=None, oracle: bool = True):
+    """Every configuration at full size, one record each: the GPU forward (back-to-back
+    calls, HIP events on the current stream) against its bound, the fp64 oracle's
+    full forward timed on the host cores, the worst |gpu - oracle| / (1 + |oracle|)
+    over every element of Q, K and V with where it occurs (the oracle's outputs are the
+    parity reference of this run), and SHA-256 digests of the seeded inputs.
+    `headline` = (workload name, seconds per forward, (q, k, v)) reuses the headline's
+    own timing and outputs instead of running it again."""
+    import numpy as np
     import torch
     res = {}
-    # the five workloads, then two mid-size batches on their shapes: 512 tokens of the GQA
-    # prefill shape (the prefill kernel's split-K form) and 128 sequences of the decode step
-    # (one launch of the decode kernel's 128-token form)
+    for wl in workloads.WORKLOADS.values():
+        inp = workloads.make_inputs(wl)
+        entry = {"tokens": wl.tokens,
+                 "sha256_16": {k: workloads.digest(inp[k]) for k in ("x", "w_norm", "w_qkv", "bias", "pos")}}
+        if headline is not None and headline[0] == wl.name:
+            sec, outs, variant = headline[1], headline[2], headline[3]
+            entry["timing"] = "the headline's own timed forwards"
+        else:
+            bufs = device_inputs(wl, inp)
+            with qkv.Plan.for_workload(wl) as plan:
+                variant = plan.variant(wl.tokens)
+                _, sec = time_forward(plan, bufs, steps, warmup)
+            outs = bufs[5:]
+            del bufs
+        flops, nbytes = wl.flops(), wl.algorithmic_bytes()
+        entry.update({"variant": variant, "us": round(sec * 1e6, 2), "tokens_per_s": round(wl.tokens / sec, 1),
+                      "tflops": round(flops / sec / 1e12, 3), "hbm_GBps": round(nbytes / sec / 1e9, 1)})
+        if wl.tokens > 256:
+            peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+            entry["mfma_frac"] = round(flops / sec / 1e12 / peak, 4)
+        elif wl.dtype == "bf16":
+            entry["hbm_frac_warm"] = round(nbytes / sec / 1e9 / PEAK_HBM_GBS, 4)
+            entry.setdefault("timing", "weight warm in the last-level cache (the decode object streams it "
+                                       "from HBM)")
+        else:
+            entry.setdefault("timing", "launch-bound (one fp32 kernel with the row reduction fused in)")
+        if oracle:
+            ref, osec = _oracle_forward(wl, inp)
+            tol = 1e-4 if wl.dtype == "fp32" else 2e-2
+            worst = None
+            for name, g, r in zip("QKV", outs, ref):
+                err, t, c = _worst_ratio(g.to("cpu", torch.float64).numpy(), r)
+                if worst is None or err > worst[0]:
+                    worst = (err, name, t, c)
+            entry["oracle"] = {"seconds": round(osec, 3), "seconds_exact": osec, "cores": _oracle_threads(),
+                               "tokens_per_s": round(wl.tokens / osec, 1),
+                               "gflops_fp64": round(flops / osec / 1e9, 2)}
+            entry["parity"] = {"max_ratio": float(f"{worst[0]:.4e}"), "tensor": worst[1], "t": worst[2],
+                               "column": worst[3], "tol": tol, "ok": bool(worst[0] <= tol),
+                               "compared": "every element of Q, K and V against the oracle's full forward"}
+            del ref
+        res[wl.name] = entry
+        del outs
+        torch.cuda.empty_cache()
+    return res
+
+
+def other_workloads_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
+    """Two mid-size batches on the configurations' shapes, back-to-back calls timed with
+    HIP events on the current stream: 512 tokens of the GQA prefill shape (the prefill
+    kernel's split-K form) and 128 sequences of the decode step (one launch of the
+    decode kernel's 128-token form)."""
+    import torch
+    res = {}
     extra = [workloads.BY_NAME["llama3_8b_gqa_prefill"].with_tokens(1, 512),
              workloads.BY_NAME["gqa_decode"].with_tokens(128, 1)]
-    for wl in list(workloads.WORKLOADS.values()) + extra:
-        if wl.name == skip:
-            continue
+    for wl in extra:
         inp = workloads.make_inputs(wl)
         bufs = device_inputs(wl, inp)
         with qkv.Plan.for_workload(wl) as plan:
             variant = plan.variant(wl.tokens)
             _, sec = time_forward(plan, bufs, steps, warmup)
         flops, nbytes = wl.flops(), wl.algorithmic_bytes()
-        entry = {"tokens": wl.tokens, "variant": variant, "us": round(sec * 1e6, 2),
-                 "tokens_per_s": round(wl.tokens / sec, 1), "tflops": round(flops / sec / 1e12, 3),
-                 "hbm_GBps": round(nbytes / sec / 1e9, 1)}
-        if wl.tokens > 256:
-            peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
-            entry["mfma_frac"] = round(flops / sec / 1e12 / peak, 4)
-        elif wl.dtype == "bf16":
-            entry["timing"] = "weight warm in the last-level cache (see the decode object for HBM-cold)"
-        else:
-            entry["timing"] = "launch-bound (one fp32 kernel with the row reduction fused in)"
-        res[wl.name] = entry
+        res[wl.name] = {"tokens": wl.tokens, "variant": variant, "us": round(sec * 1e6, 2),
+                        "tokens_per_s": round(wl.tokens / sec, 1), "tflops": round(flops / sec / 1e12, 3),
+                        "hbm_GBps": round(nbytes / sec / 1e9, 1)}
         del bufs
         torch.cuda.empty_cache()
     return res
+
+
+def prepass_leg(qkv, wl, bufs, steps: int = 30, warmup: int = 5):
+    """The same forward through a plan with the opt-in pre-pass form
+    (QKV_PLAN_PREFILL_PREPASS): a pre-pass writes bf16(x * w_norm) to HBM and the MFMA
+    kernel streams it back, two launches.  Timed here beside the default single launch,
+    which never writes the normalised activations."""
+    with qkv.Plan.for_workload(wl, prefill_prepass=True) as plan:
+        _, sec = time_forward(plan, bufs, steps, warmup)
+    return sec
 
 
 def zero_weight_leg(plan, bufs, steps: int = 30, warmup: int = 5):
@@ -418,29 +514,17 @@ def zero_weight_leg(plan, bufs, steps: int = 30, warmup: int = 5):
     return sec
 
 
-def cpu_baseline_leg(wl, inp):
-    """The fp64 oracle, as it stands, on the host cores: one full forward."""
-    import numpy as np
-    from oracle import qkv_oracle
-    try:
-        import threadpoolctl
-        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
-    except Exception:
-        threads = os.cpu_count() or 1
-    to64 = lambda t: None if t is None else t.to(dtype=__import__("torch").float64).numpy()
-    args = (to64(inp["x"]), to64(inp["w_norm"]), to64(inp["w_qkv"]), to64(inp["bias"]),
-            inp["pos"].numpy().astype(np.int64), wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.eps,
-            wl.rope_theta)
-    t0 = time.perf_counter()
-    qkv_oracle.qkv_forward(*args)
-    dt = time.perf_counter() - t0
+def cpu_baseline_leg(wl, inp, seconds=None):
+    """The fp64 oracle, as it stands, on the host cores: one full forward (`seconds`:
+    the configurations leg already timed that same forward in this run)."""
+    dt = seconds if seconds is not None else _oracle_forward(wl, inp)[1]
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
             cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
     except OSError:
         pass
-    return {"value": round(wl.tokens / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(wl.tokens / dt, 1), "unit": "tokens/s", "cores": _oracle_threads(), "kind": "oracle",
             "cpu_model": cpu,
             "sample": f"one full forward of {wl.name} ({wl.tokens} tokens) in fp64, {dt:.2f} s",
             "seconds": round(dt, 3)}
@@ -451,11 +535,13 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama7b_prefill")
+    ap.add_argument("--workload", default="qwen7b_prefill_bias",
+                    help="headline workload (default: the largest configuration, the Qwen-7B-shaped prefill)")
     ap.add_argument("--tokens", type=int, default=0,
                     help="run the workload's shape at this many tokens (one sequence) instead of its own")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
-    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle (the headline's baseline and each configuration's oracle and parity)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the key/value-cache, gated-MLP, backward, other-workload and zero-weight legs "
                          "(time only the workload's own forward)")
@@ -496,14 +582,19 @@ def main() -> int:
     print(f"[bench] {wl.name}: T={wl.tokens} H={wl.hidden} N={wl.n_total} variant={variant} "
           f"steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     wall, kernel_s = time_forward(plan, bufs, args.steps, args.warmup)
+    # the headline's outputs, kept for its parity check against the oracle (the legs
+    # below reuse the output buffers)
+    head_out = None if args.no_extra or args.tokens else tuple(t.to("cpu") for t in bufs[5:])
     cold = None
     if wl.tokens > 256 and not args.no_cold:
         cold = time_forward_cold(plan, bufs)
     cache_s = None if args.no_extra else time_forward_kv_cache(qkv, wl, plan, bufs, args.steps, args.warmup)
-    zero_s = None
+    zero_s = prepass_s = None
     if not args.no_extra and wl.tokens > 256 and wl.dtype == "bf16":
         zero_s = zero_weight_leg(plan, bufs)
     plan.close()
+    if not args.no_extra and variant == "prefill":
+        prepass_s = prepass_leg(qkv, wl, bufs)
 
     flops = wl.flops()
     nbytes = wl.algorithmic_bytes()
@@ -514,7 +605,8 @@ def main() -> int:
         bound, achieved, unit = "mfma", flops / kernel_s / 1e12, "TFLOP/s"
     traffic = measured_traffic(wl.name)
     # the launches of one forward, all inside the HIP-event window that gives kernel_us
-    kernels = {"prefill": "prenorm_kernel + prefill_kernel", "prefill_split": "prefill_kernel (split-K form)",
+    kernels = {"prefill": "prefill_wide_kernel (one launch, normalise-on-load)",
+               "prefill_split": "prefill_kernel (split-K form)",
                "decode": "decode_kernel", "generic": "generic kernel"}.get(variant, variant)
     out = {
         "metric": METRIC,
@@ -545,6 +637,14 @@ def main() -> int:
                            "time_vs_dense": round(cache_s / kernel_s, 4),
                            "cache": "K and V rows written to slot = sequence's first row + position mod C "
                                     "of [batch x C, kv_heads*head_dim] caches, C = max(4096, seq_len)"}
+    if prepass_s is not None:
+        out["prefill_prepass_opt_in"] = {
+            "us": round(prepass_s * 1e6, 2), "time_vs_default": round(prepass_s / kernel_s, 4),
+            "tflops": round(flops / prepass_s / 1e12, 2),
+            "extra_hbm_bytes": 2 * wl.tokens * wl.hidden * 2,
+            "note": "QKV_PLAN_PREFILL_PREPASS: pre-pass writes bf16(x * w_norm) to HBM, the 256 x 256 MFMA kernel "
+                    "streams it back (two launches); the headline single launch never writes the normalised "
+                    "activations"}
     if zero_s is not None:
         out["prefill_zero_weight"] = {
             "us": round(zero_s * 1e6, 2), "time_vs_seeded": round(zero_s / kernel_s, 4),
@@ -565,16 +665,25 @@ def main() -> int:
         print("[bench] gated-MLP leg", file=sys.stderr, flush=True)
         out["swiglu"] = swiglu_leg(qkv, workloads)
         print("[bench] backward leg", file=sys.stderr, flush=True)
-        out["backward"] = backward_leg(qkv, workloads, wl, bufs)
-        del bufs
+        bwl = workloads.BY_NAME["llama7b_prefill"]
+        bbufs = device_inputs(bwl, workloads.make_inputs(bwl))
+        out["backward"] = backward_leg(qkv, workloads, bwl, bbufs)
+        del bbufs
         torch.cuda.empty_cache()
         print("[bench] unfused comparison leg", file=sys.stderr, flush=True)
         out["unfused"] = unfused_leg(qkv, workloads)
         print("[bench] other workloads leg", file=sys.stderr, flush=True)
-        out["other_workloads"] = other_workloads_leg(qkv, workloads, skip=wl.name)
+        out["other_workloads"] = other_workloads_leg(qkv, workloads)
+    del bufs
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        print("[bench] configurations leg (GPU, oracle, parity)", file=sys.stderr, flush=True)
+        head = None if head_out is None else (wl.name, kernel_s, head_out, variant)
+        out["configs"] = configs_leg(qkv, workloads, headline=head, oracle=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline leg", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline_leg(wl, inp)
+        own = out.get("configs", {}).get(wl.name, {}).get("oracle") if head_out is not None else None
+        out["cpu_baseline"] = cpu_baseline_leg(wl, inp, seconds=None if own is None else own["seconds_exact"])
     print(json.dumps(out), flush=True)
     return 0
 

@@ -39,9 +39,9 @@
  * buffers alive until the work queued on `stream` has finished.  A plan owns only
  * its device scratch (per-token inverse RMS values, decode partial sums and
  * counters, the split-K prefill form's partial tiles -- up to 67 MB -- and counters,
- * the prefill pre-pass's bf16 normalise-on-load products -- max_tokens * hidden * 2
- * bytes -- and the rotary frequency table), allocated on the device that is current
- * when the plan is created and freed by qkv_plan_destroy.
+ * the rotary frequency table, and with QKV_PLAN_PREFILL_PREPASS the pre-pass's bf16
+ * products -- ceil(max_tokens / 256) * 256 * hidden * 2 bytes), allocated on the
+ * device that is current when the plan is created and freed by qkv_plan_destroy.
  *
  * Errors: every call returns a status code; nothing is thrown across the ABI.
  * Arguments are validated before any HIP call is made.
@@ -71,9 +71,9 @@ typedef enum qkv_dtype {
 /* Kernel path a forward of a given token count runs on (see qkv_plan_variant). */
 typedef enum qkv_variant {
   QKV_VARIANT_GENERIC = 0,  /* fp32 FMA tiles: any supported shape, both dtypes        */
-  QKV_VARIANT_PREFILL = 1,  /* two launches: a pre-pass writes bf16(x * w_norm) and
-                               1/rms per row, then the bf16 MFMA GEMM streams them
-                               with the weight and applies 1/rms, bias and rotation     */
+  QKV_VARIANT_PREFILL = 1,  /* one bf16 MFMA launch normalising the activations as
+                               they are loaded, applying 1/rms, bias and rotation
+                               (two launches with QKV_PLAN_PREFILL_PREPASS)             */
   QKV_VARIANT_DECODE = 2,   /* bf16 MFMA weight-streaming kernel for small token counts:
                                up to 192 (or 256) tokens, one launch per 128 tokens     */
   QKV_VARIANT_PREFILL_SPLIT = 3  /* the prefill kernel with the hidden dimension split over
@@ -93,7 +93,17 @@ typedef struct qkv_plan_desc {
   int32_t has_bias;       /* 0 or 1                                                      */
   double eps;             /* >= 0, finite; added to the mean square inside the sqrt      */
   double rope_theta;      /* > 0, finite; rotary base                                    */
+  int32_t flags;          /* 0, or QKV_PLAN_PREFILL_PREPASS                              */
 } qkv_plan_desc;
+
+/* Plan flag: plain prefill forwards (QKV_VARIANT_PREFILL) run as two launches, a pre-pass
+ * that writes bf16(x * w_norm) and each row's 1/rms to plan scratch
+ * (ceil(max_tokens / 256) * 256 * hidden * 2 bytes, allocated at plan creation), then the
+ * 256 x 256 MFMA kernel streaming those activations from HBM.  Without the flag (the
+ * default) the normalised activations never leave the chip: one launch normalises each
+ * row as it is loaded.  The flag exists to measure the trade-off; results agree within
+ * the parity bar, not bit for bit. */
+#define QKV_PLAN_PREFILL_PREPASS 1
 
 /* Validate `desc`, pick the kernel variants, allocate the plan's device scratch on
  * the current device and return an opaque handle in *out_plan.

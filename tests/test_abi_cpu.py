@@ -67,6 +67,8 @@ def _create(**over):
     (dict(eps=float("nan")), qkv.QKV_ERR_INVALID_ARG),
     (dict(rope_theta=0.0), qkv.QKV_ERR_INVALID_ARG),
     (dict(rope_theta=float("inf")), qkv.QKV_ERR_INVALID_ARG),
+    (dict(flags=2), qkv.QKV_ERR_INVALID_ARG),
+    (dict(flags=-1), qkv.QKV_ERR_INVALID_ARG),
     (dict(hidden=60), qkv.QKV_ERR_UNSUPPORTED),
     (dict(head_dim=6), qkv.QKV_ERR_UNSUPPORTED),
     (dict(max_tokens=1 << 40), qkv.QKV_ERR_UNSUPPORTED),
@@ -176,3 +178,4 @@ def test_token_limit_is_exact(shape):
     assert st in (qkv.QKV_OK, qkv.QKV_ERR_HIP)
     if st == qkv.QKV_OK:
         assert qkv.load_library().qkv_plan_destroy(h) == qkv.QKV_OK
+

@@ -72,6 +72,9 @@ CASES = {
                                                head_dim=64)),
     "fp32_d256": (workloads.WORKLOADS[1], dict(batch=1, seq=40, hidden=128, num_q_heads=2, num_kv_heads=1,
                                                 head_dim=256)),
+    # the shape the benchmark times the backward on: Llama-7B, 4 x 2048 tokens, every
+    # element of every gradient against the oracle's full chain rule
+    "llama7b_full": (workloads.WORKLOADS[2], {}),
 }
 
 

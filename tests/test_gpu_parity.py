@@ -53,13 +53,16 @@ def test_decode_full():
     print(P.assert_parity(got, ref, P.TOL["bf16"], wl.name))
 
 
+@pytest.mark.parametrize("prepass", [False, True], ids=["one_launch", "prepass_opt_in"])
 @pytest.mark.parametrize("cid", [2, 3, 5])
-def test_prefill_full_size_sampled_rows(cid):
-    """Full-size forward in the benchmark's launch configuration; the oracle evaluates
-    a sample of rows (ends, tile edges, random) one token at a time."""
+def test_prefill_full_size_sampled_rows(cid, prepass):
+    """Full-size forward in the benchmark's launch configuration (and in the opt-in
+    pre-pass form); the oracle evaluates a sample of rows (ends, every tile edge,
+    random) one token at a time."""
     wl = workloads.WORKLOADS[cid]
     inp = workloads.make_inputs(wl)
-    with qkv.Plan.for_workload(wl) as plan:
+    with qkv.Plan.for_workload(wl, prefill_prepass=prepass) as plan:
+        assert plan.variant(wl.tokens) == "prefill"
         got = run(plan, inp)
     for t in got:
         assert torch.isfinite(t).all(), "non-finite output"
@@ -404,9 +407,9 @@ def test_decode_two_full_chunks():
 
 
 def test_plan_reuse_across_token_counts():
-    """One plan serving forwards of different sizes in turn (plain prefill with its pre-pass
-    scratch, split-K prefill, decode, and plain again): each bit-identical to the same forward
-    through a fresh plan of its own size."""
+    """One plan serving forwards of different sizes in turn (plain prefill, split-K prefill
+    with its partial tiles, decode with its partial sums, and plain again): each
+    bit-identical to the same forward through a fresh plan of its own size."""
     base = workloads.WORKLOADS[3]
     with qkv.Plan.for_workload(base.with_tokens(1, 2048)) as plan:
         for T, variant in ((2048, "prefill"), (1537, "prefill"), (300, "prefill_split"), (64, "decode"),
@@ -438,8 +441,8 @@ def test_variant_names():
 
 @pytest.mark.parametrize("cid,T,variant", [(3, 300, "prefill_split"), (3, 2048, "prefill"), (4, 150, "decode")])
 def test_graph_replays(cid, T, variant):
-    """A forward captured in a HIP graph (split-K prefill; plain prefill, pre-pass then MFMA
-    kernel; decode over a 128-token and a 22-token chunk): each of several replays, with
+    """A forward captured in a HIP graph (split-K prefill; plain prefill, one launch; decode
+    over a 128-token and a 22-token chunk): each of several replays, with
     eager forwards of other inputs in between, writes exactly the eager result; the kernels
     leave their arrival counters at zero for the next call."""
     wl = workloads.WORKLOADS[cid].with_tokens(1, T) if cid == 3 else workloads.WORKLOADS[cid].with_tokens(T, 1)

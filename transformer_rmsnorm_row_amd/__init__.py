@@ -55,7 +55,11 @@ class PlanDesc(ctypes.Structure):
         ("has_bias", ctypes.c_int32),
         ("eps", ctypes.c_double),
         ("rope_theta", ctypes.c_double),
+        ("flags", ctypes.c_int32),
     ]
+
+
+QKV_PLAN_PREFILL_PREPASS = 1
 
 
 class QKVError(RuntimeError):
@@ -149,7 +153,7 @@ class Plan:
 
     def __init__(self, *, max_tokens: int, hidden: int, num_q_heads: int, num_kv_heads: int,
                  head_dim: int, dtype: torch.dtype = torch.bfloat16, has_bias: bool = False,
-                 eps: float = 1e-6, rope_theta: float = 10000.0):
+                 eps: float = 1e-6, rope_theta: float = 10000.0, prefill_prepass: bool = False):
         self._lib = load_library()
         self.dtype = dtype
         self.hidden = hidden
@@ -161,16 +165,17 @@ class Plan:
         self.n_q = num_q_heads * head_dim
         self.n_kv = num_kv_heads * head_dim
         self.desc = PlanDesc(max_tokens, hidden, num_q_heads, num_kv_heads, head_dim,
-                             _dtype_code(dtype), int(bool(has_bias)), float(eps), float(rope_theta))
+                             _dtype_code(dtype), int(bool(has_bias)), float(eps), float(rope_theta),
+                             QKV_PLAN_PREFILL_PREPASS if prefill_prepass else 0)
         handle = ctypes.c_void_p()
         _check(self._lib.qkv_plan_create(ctypes.byref(self.desc), ctypes.byref(handle)), "qkv_plan_create")
         self._handle = handle
 
     @classmethod
-    def for_workload(cls, wl, max_tokens: Optional[int] = None) -> "Plan":
+    def for_workload(cls, wl, max_tokens: Optional[int] = None, prefill_prepass: bool = False) -> "Plan":
         return cls(max_tokens=max_tokens or wl.tokens, hidden=wl.hidden, num_q_heads=wl.num_q_heads,
                    num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim, dtype=wl.torch_dtype,
-                   has_bias=wl.has_bias, eps=wl.eps, rope_theta=wl.rope_theta)
+                   has_bias=wl.has_bias, eps=wl.eps, rope_theta=wl.rope_theta, prefill_prepass=prefill_prepass)
 
     @property
     def handle(self) -> ctypes.c_void_p:

@@ -78,6 +78,11 @@ hipError_t launch_inv_rms(const void* x, float* inv_rms, int T, int H, float eps
 hipError_t launch_generic(const ForwardArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream);
 bool prefill_supports(int H, int N, int Nq, int Nkv, int d);
+// Single-launch normalise-on-load prefill on 128 x 512 tiles with 16 x 16 x 32 MFMAs
+// (prefill_wide.hip): the plain prefill forward's kernel for head sizes 64/128/256, N a
+// multiple of 512 and H of 128.
+hipError_t launch_prefill_wide(const ForwardArgs& a, hipStream_t stream);
+bool prefill_wide_supports(int H, int N, int Nq, int Nkv, int d);
 // The split-K form of the prefill kernel (two K slices per 256 x 256 tile, partial
 // tiles added by the last-arriving workgroup) is used up to this many tiles, one arrival
 // counter each.

@@ -1,13 +1,17 @@
-// bf16 MFMA prefill kernel for gfx950: RMS row reduction, normalise-on-load QKV
-// projection, bias and rotate-half rotary embedding in one launch, Q/K/V written once.
+// bf16 MFMA prefill kernel for gfx950 on 256 x 256 tiles: RMS row reduction,
+// normalise-on-load QKV projection, bias and rotate-half rotary embedding, Q/K/V
+// written once.  It serves the prefill shapes the 128 x 512 kernel of prefill_wide.hip
+// does not take, the split-K form for token counts too small to fill the chip, the gated
+// MLP epilogue, and the opt-in pre-normalised form (activations normalised once into a
+// plan buffer by a pre-pass, then loaded like the weight).
 //
 // The method is the fused RMSNorm + QKV projection + RoPE kernel of the page
 // "Liger-Kernel底层优化：新一代内核级推理加速引擎介绍" (section
 // "融合内核是如何工作的？来看一段简化版实现", and the fused-kernel list that names
 // "Fused RMSNorm + QKV Projection + RoPE"): the sum of squares over the hidden size
-// gives each token's 1/rms, the normalised activations exist only inside the
-// kernel, the bias is added to each dot product, and each rotation pair
-// (i, i + head_dim/2) is turned by the position's angle before the single store.
+// gives each token's 1/rms, the bias is added to each dot product, and each rotation pair
+// (i, i + head_dim/2) is turned by the position's angle before the single store.  In the
+// default form the normalised activations exist only inside the kernel.
 //
 // gfx950 design (the listing's one-thread-per-feature loop is not used):
 //   * 256 x 256 output tile per 512-thread workgroup (8 waves, two per SIMD).  Wave

@@ -34,7 +34,7 @@ struct Plan {
   float* kpart;       // split-K prefill: partial tiles
   uint32_t* kcount;   // split-K prefill: per-tile arrival counters
   int kpart_units;    // partial tiles kpart holds
-  void* xw;           // prefill: bf16(x * w_norm) from the pre-pass, max_tokens rounded up to 256 rows
+  void* xw;           // QKV_PLAN_PREFILL_PREPASS: bf16(x * w_norm) from the pre-pass, max_tokens rounded up to 256 rows
   // backward scratch, allocated by the first qkv_backward through the plan
   void* bwd_gy;         // [max_tokens, N] plan dtype
   void* bwd_act;        // [max_tokens, H] plan dtype
@@ -65,6 +65,7 @@ qkv_status check_desc(const qkv_plan_desc* d) {
   if (d->has_bias != 0 && d->has_bias != 1) return QKV_ERR_INVALID_ARG;
   if (!std::isfinite(d->eps) || d->eps < 0.0) return QKV_ERR_INVALID_ARG;
   if (!std::isfinite(d->rope_theta) || d->rope_theta <= 0.0) return QKV_ERR_INVALID_ARG;
+  if ((d->flags & ~QKV_PLAN_PREFILL_PREPASS) != 0) return QKV_ERR_INVALID_ARG;
   if (d->hidden % 8 != 0) return QKV_ERR_UNSUPPORTED;
   if (d->head_dim % 8 != 0) return QKV_ERR_UNSUPPORTED;
   const int64_t elem = d->dtype == QKV_BF16 ? 2 : 4;
@@ -210,13 +211,19 @@ qkv_status launch_forward(Plan* pl, int64_t num_tokens, const void* x, const voi
   hipError_t e;
   switch (choose_variant(pl, num_tokens)) {
     case QKV_VARIANT_PREFILL:
-      // pre-pass: bf16(x * w_norm) and 1/rms per row into plan scratch; the MFMA kernel
-      // then streams the activations global -> LDS like the weight
-      e = qkv::launch_prenorm(x, w_norm, pl->xw, pl->inv_rms, a.T, a.H, a.eps, s);
-      if (e != hipSuccess) break;
-      a.x = pl->xw;
-      a.prenormed = true;
-      e = qkv::launch_prefill(a, s);
+      if (pl->xw) {
+        // pre-pass form (QKV_PLAN_PREFILL_PREPASS): bf16(x * w_norm) and 1/rms per row
+        // into plan scratch; the MFMA kernel then streams the activations like the weight
+        e = qkv::launch_prenorm(x, w_norm, pl->xw, pl->inv_rms, a.T, a.H, a.eps, s);
+        if (e != hipSuccess) break;
+        a.x = pl->xw;
+        a.prenormed = true;
+        e = qkv::launch_prefill(a, s);
+      } else if (qkv::prefill_wide_supports(a.H, a.N, a.Nq, a.Nkv, a.d)) {
+        e = qkv::launch_prefill_wide(a, s);  // one launch, normalise-on-load
+      } else {
+        e = qkv::launch_prefill(a, s);  // one launch, the 256 x 256 kernel's normalise-on-load form
+      }
       break;
     case QKV_VARIANT_PREFILL_SPLIT:  // the launcher makes the same split choice
       e = qkv::launch_prefill(a, s);
@@ -293,7 +300,8 @@ qkv_status qkv_plan_create(const qkv_plan_desc* desc, qkv_plan* out_plan) {
     // most CUs idle) and one arrival counter per tile (zeroed once; the kernel leaves
     // them at zero after every forward)
     pl->kpart_units = qkv::prefill_split_units((int)desc->max_tokens, pl->N);
-    ok = hipMalloc(&pl->xw, (size_t)(desc->max_tokens + 255) / 256 * 256 * desc->hidden * 2) == hipSuccess &&
+    ok = ((desc->flags & QKV_PLAN_PREFILL_PREPASS) == 0 ||
+          hipMalloc(&pl->xw, (size_t)(desc->max_tokens + 255) / 256 * 256 * desc->hidden * 2) == hipSuccess) &&
          hipMalloc(&pl->kpart, sizeof(float) * qkv::prefill_split_floats(pl->kpart_units)) == hipSuccess &&
          hipMalloc(&pl->kcount, sizeof(uint32_t) * qkv::kPrefillSplitMaxTiles) == hipSuccess &&
          hipMemset(pl->kcount, 0, sizeof(uint32_t) * qkv::kPrefillSplitMaxTiles) == hipSuccess &&
