@@ -155,6 +155,32 @@ qkv_status qkv_forward_kv_cache(qkv_plan plan, int64_t num_tokens,
                                 const int32_t* slots, int64_t cache_rows,
                                 void* q, void* k_cache, void* v_cache, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc: the forward of qkv_forward
+ * without a plan.  `desc` describes the layer exactly as for qkv_plan_create
+ * (validated the same way; T = num_tokens must satisfy 1 <= T <= desc->max_tokens;
+ * desc->flags must be 0, since the pre-pass form needs plan scratch, else
+ * QKV_ERR_UNSUPPORTED), and every other argument is as for qkv_forward.  Nothing is allocated: the call's
+ * scratch (its rotary table and the decode kernel's partial sums and arrival counters)
+ * lives in one file-scope device array of the library, 16,912,384 bytes per GPU,
+ * reserved on every GPU the library runs on until the process ends.  Each call first
+ * queues a one-workgroup kernel that writes its rotary table and zeroes the counters,
+ * then the forward's kernels: the decode kernel for up to 256 tokens (consecutive
+ * launches of up to 128) on shapes it supports, else the single-launch
+ * normalise-on-load prefill kernel (never its split-K form, whose partial tiles would
+ * not fit), else the generic kernel; results match qkv_forward's within the same
+ * tolerance (bit for bit where both run the same kernel).
+ * All calls on one GPU share that array: two calls that overlap in time on one GPU
+ * (different streams, or different host threads on one stream without ordering) race
+ * and may return wrong results; queue them on one stream, one after the other.
+ * head_dim above 512 (a table beyond the array's slot) returns QKV_ERR_UNSUPPORTED;
+ * argument errors return QKV_ERR_INVALID_ARG before any HIP call; a failed launch or
+ * symbol lookup returns QKV_ERR_HIP. */
+qkv_status qkv_forward_noalloc(const qkv_plan_desc* desc, int64_t num_tokens,
+                               const void* x, const void* w_norm, const void* w_qkv,
+                               const void* bias, const int32_t* pos,
+                               void* q, void* k, void* v, void* stream);
+
 /* Queue only the row reduction of the chain: inv_rms[t] = 1/sqrt(mean_k x[t,k]^2 + eps)
  * as fp32 for t < num_tokens, into the caller's device buffer `inv_rms` (4-byte
  * aligned).  Same argument rules, asynchrony and errors as qkv_forward. */

@@ -179,3 +179,37 @@ def test_token_limit_is_exact(shape):
     if st == qkv.QKV_OK:
         assert qkv.load_library().qkv_plan_destroy(h) == qkv.QKV_OK
 
+
+def _noalloc(desc, T, ptrs=None, bias=None):
+    lib = qkv.load_library()
+    p = ptrs if ptrs is not None else [16] * 8  # x, w_norm, w_qkv, pos, q, k, v (16-byte aligned dummies)
+    return lib.qkv_forward_noalloc(None if desc is None else ctypes.byref(desc), T, p[0], p[1], p[2], bias, p[3],
+                                   p[4], p[5], p[6], None)
+
+
+def test_noalloc_rejects_bad_arguments_before_any_hip_call():
+    """qkv_forward_noalloc validates the descriptor and every argument before it looks
+    up its device array or launches anything (these calls run without a GPU)."""
+    good = dict(max_tokens=16, hidden=64, num_q_heads=4, num_kv_heads=4, head_dim=16, dtype=0, has_bias=0,
+                eps=1e-6, rope_theta=1e4)
+    d = qkv.PlanDesc(**good)
+    assert _noalloc(None, 4) == qkv.QKV_ERR_INVALID_ARG
+    assert _noalloc(qkv.PlanDesc(**{**good, "head_dim": 15}), 4) == qkv.QKV_ERR_INVALID_ARG
+    assert _noalloc(qkv.PlanDesc(**{**good, "hidden": 60}), 4) == qkv.QKV_ERR_UNSUPPORTED
+    assert _noalloc(d, 0, ptrs=[None] * 8) == qkv.QKV_OK           # T == 0 touches nothing
+    assert _noalloc(d, -1) == qkv.QKV_ERR_INVALID_ARG
+    assert _noalloc(d, 17) == qkv.QKV_ERR_INVALID_ARG              # above max_tokens
+    for i in range(7):
+        ptrs = [16] * 8
+        ptrs[i] = None
+        assert _noalloc(d, 4, ptrs=ptrs) == qkv.QKV_ERR_INVALID_ARG
+        ptrs[i] = 24 if i != 3 else 2                                  # misaligned
+        assert _noalloc(d, 4, ptrs=ptrs) == qkv.QKV_ERR_INVALID_ARG
+    assert _noalloc(d, 4, bias=16) == qkv.QKV_ERR_INVALID_ARG       # bias on a plan without one
+    db = qkv.PlanDesc(**{**good, "has_bias": 1})
+    assert _noalloc(db, 4) == qkv.QKV_ERR_INVALID_ARG              # missing bias
+    # the pre-pass form needs plan scratch
+    assert _noalloc(qkv.PlanDesc(**{**good, "flags": qkv.QKV_PLAN_PREFILL_PREPASS}), 4) == qkv.QKV_ERR_UNSUPPORTED
+    # a rotary table larger than its slot in the device array
+    big = qkv.PlanDesc(**{**good, "hidden": 2048, "num_q_heads": 1, "num_kv_heads": 1, "head_dim": 1040})
+    assert _noalloc(big, 4) == qkv.QKV_ERR_UNSUPPORTED

@@ -36,6 +36,7 @@ EXPORTS = {
     "qkv_rope": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp]),
     "qkv_forward_unfused": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qkv_head_norm_rope": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp]),
+    "qkv_forward_noalloc": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qkv_plan_variant": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)]),
     "qkv_plan_destroy": (ctypes.c_int, [_vp]),
     "qkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -133,6 +134,26 @@ def swiglu_forward(x: torch.Tensor, w_norm: torch.Tensor, w_gate_up: torch.Tenso
     _check(lib.qkv_swiglu_forward(T, H, I, _dtype_code(x.dtype), float(eps), _ptr(x), _ptr(w_norm),
                                   _ptr(w_gate_up), _ptr(out), _stream_handle(stream)), "qkv_swiglu_forward")
     return out
+
+
+def forward_noalloc(desc: "PlanDesc", x: torch.Tensor, w_norm: torch.Tensor, w_qkv: torch.Tensor,
+                    bias: Optional[torch.Tensor], pos: torch.Tensor,
+                    out: Tuple[torch.Tensor, torch.Tensor, torch.Tensor],
+                    stream: Optional[torch.cuda.Stream] = None):
+    """qkv_forward_noalloc: the forward of a layer described by ``desc`` (a PlanDesc)
+    into the caller's ``out = (q, k, v)``, with no plan and no device allocation (its
+    scratch is the library's own device array).  Tensors must be contiguous, on the GPU
+    and of the layer's shapes; the library validates the rest."""
+    lib = load_library()
+    q, k, v = out
+    for name, t in (("x", x), ("w_norm", w_norm), ("w_qkv", w_qkv), ("pos", pos), ("q", q), ("k", k), ("v", v),
+                    ("bias", bias)):
+        if t is not None and (not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    _check(lib.qkv_forward_noalloc(ctypes.byref(desc), x.shape[0], _ptr(x), _ptr(w_norm), _ptr(w_qkv), _ptr(bias),
+                                   _ptr(pos), _ptr(q), _ptr(k), _ptr(v), _stream_handle(stream)),
+           "qkv_forward_noalloc")
+    return q, k, v
 
 
 def ring_slots(pos: torch.Tensor, capacity: int, first_row: int = 0) -> torch.Tensor:

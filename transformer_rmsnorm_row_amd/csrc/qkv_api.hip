@@ -15,6 +15,10 @@
 #include "launch.h"
 #include "unfused.h"
 
+// Device scratch of qkv_forward_noalloc (layout and size next to that entry point).
+constexpr size_t kNoAllocScratchBytes = 4096 + (size_t)256 * (128 * 128 + 128) * sizeof(float);
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 namespace {
 
 constexpr uint64_t kPlanMagic = 0x514b564d49333535ull;  // "QKVMI355"
@@ -257,6 +261,59 @@ qkv_status launch_forward(Plan* pl, int64_t num_tokens, const void* x, const voi
   return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
 }
 
+// ---- no-allocation forward: its scratch is a file-scope device array ----
+//
+// Layout of `scratch` (one copy per GPU, kept until the process ends):
+//   [0, 2 KB)        rotary frequency table, up to 256 doubles (head_dim <= 512)
+//   [2 KB, 3 KB)     decode arrival counters, one per 128-column head (up to 256)
+//   [4 KB, end)      decode partial sums: at most 256 units of 128 tokens x 128 columns
+//                    plus 128 sums of squares each (the decode kernel runs at most one unit
+//                    per CU, so every supported shape fits)
+constexpr size_t kNoAllocRevOffset = 0, kNoAllocRevMax = 256;
+constexpr size_t kNoAllocCountOffset = 2048, kNoAllocMaxHeads = 256;
+constexpr size_t kNoAllocPartOffset = 4096;
+constexpr size_t kNoAllocPartFloats = 256 * (128 * 128 + 128);
+constexpr size_t kNoAllocBytes = kNoAllocPartOffset + kNoAllocPartFloats * sizeof(float);
+static_assert(kNoAllocRevOffset + kNoAllocRevMax * sizeof(double) <= kNoAllocCountOffset, "table fits");
+static_assert(kNoAllocCountOffset + kNoAllocMaxHeads * sizeof(uint32_t) <= kNoAllocPartOffset, "counters fit");
+static_assert(kNoAllocBytes == kNoAllocScratchBytes, "the array holds the layout");
+
+struct RevTable {
+  double rev[kNoAllocRevMax];
+};
+
+// One workgroup: writes the call's rotary table and zeroes the decode counters, in
+// stream order before the forward's kernels (a kernel, not a memset, so the call can
+// be captured into a graph).
+__global__ __launch_bounds__(256) void noalloc_setup_kernel(RevTable tbl, int half, uint8_t* base) {
+  double* rev = reinterpret_cast<double*>(base + kNoAllocRevOffset);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(base + kNoAllocCountOffset);
+  const int i = (int)threadIdx.x;
+  if (i < half) rev[i] = tbl.rev[i];
+  if (i < (int)kNoAllocMaxHeads) cnt[i] = 0u;
+}
+
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_noalloc_mu;
+uint8_t* g_noalloc_ptr[kNoAllocMaxDevices];
+
+// The device address of `scratch` on device `dev` (current), looked up once per device.
+// In host code the array's name is only a handle for the runtime, never an address.
+qkv_status noalloc_scratch(int dev, uint8_t** out) {
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return QKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return QKV_ERR_HIP;
+    }
+    g_noalloc_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_noalloc_ptr[dev];
+  return QKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -363,6 +420,98 @@ qkv_status qkv_forward_kv_cache(qkv_plan plan, int64_t num_tokens, const void* x
   if (cache_rows >= kMaxBytes / ((int64_t)pl->Nkv * elem)) return QKV_ERR_UNSUPPORTED;
   return launch_forward(pl, num_tokens, x, w_norm, w_qkv, bias, pos, q, k_cache, v_cache, slots, (int)cache_rows,
                         stream);
+}
+
+qkv_status qkv_forward_noalloc(const qkv_plan_desc* desc, int64_t num_tokens, const void* x, const void* w_norm,
+                               const void* w_qkv, const void* bias, const int32_t* pos, void* q, void* k, void* v,
+                               void* stream) {
+  qkv_status st = check_desc(desc);
+  if (st != QKV_OK) return st;
+  if (desc->flags != 0) return QKV_ERR_UNSUPPORTED;  // the pre-pass form needs plan scratch
+  if (num_tokens == 0) return QKV_OK;
+  if (num_tokens < 0 || num_tokens > desc->max_tokens) return QKV_ERR_INVALID_ARG;
+  if (!x || !w_norm || !w_qkv || !pos || !q || !k || !v) return QKV_ERR_INVALID_ARG;
+  if ((bias != nullptr) != (desc->has_bias == 1)) return QKV_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w_norm, 16) || !aligned(w_qkv, 16) || !aligned(q, 16) || !aligned(k, 16) ||
+      !aligned(v, 16) || !aligned(pos, 4) || (bias && !aligned(bias, 16)))
+    return QKV_ERR_INVALID_ARG;
+  const int half = desc->head_dim / 2;
+  if ((size_t)half > kNoAllocRevMax) return QKV_ERR_UNSUPPORTED;  // table larger than its slot
+  const int Nq = desc->num_q_heads * desc->head_dim, Nkv = desc->num_kv_heads * desc->head_dim;
+  const int N = Nq + 2 * Nkv, H = desc->hidden, d = desc->head_dim;
+  const bool bf16 = desc->dtype == QKV_BF16;
+  const int64_t T = num_tokens;
+  // Kernel choice as for a plan without the split-K prefill form (whose partial tiles
+  // would not fit): the decode kernel up to two launches of 128 tokens when its partial
+  // sums fit the array, else the single-launch normalise-on-load prefill kernel, else
+  // the generic kernel.
+  const bool decode_fits = bf16 && qkv::decode_supports(1, H, N, Nq, Nkv, d) && (size_t)(N / 128) <= kNoAllocMaxHeads &&
+                           qkv::decode_scratch_floats(H, N) <= kNoAllocPartFloats;
+  int variant = QKV_VARIANT_GENERIC;
+  if (decode_fits && T <= kDecodeMaxTokensUnsplit &&
+      qkv::decode_supports((int)std::min<int64_t>(T, qkv::kDecodeTokens), H, N, Nq, Nkv, d))
+    variant = QKV_VARIANT_DECODE;
+  else if (bf16 && qkv::prefill_supports(H, N, Nq, Nkv, d))
+    variant = QKV_VARIANT_PREFILL;
+  if (variant == QKV_VARIANT_DECODE && qkv::decode_scratch_floats(H, N) > kNoAllocPartFloats)
+    return QKV_ERR_UNSUPPORTED;  // never reached for supported shapes; kept as the size guard
+
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return QKV_ERR_HIP;
+  uint8_t* base = nullptr;
+  st = noalloc_scratch(dev, &base);
+  if (st != QKV_OK) return st;
+
+  RevTable tbl{};
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < half; ++i) tbl.rev[i] = std::pow(desc->rope_theta, -2.0 * (double)i / (double)d) / two_pi;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  noalloc_setup_kernel<<<dim3(1), dim3(256), 0, s>>>(tbl, half, base);
+  if (hipGetLastError() != hipSuccess) return QKV_ERR_HIP;
+
+  qkv::ForwardArgs a{};
+  a.x = x;
+  a.w_norm = w_norm;
+  a.w = w_qkv;
+  a.bias = bias;
+  a.pos = pos;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.rev_freq = reinterpret_cast<const double*>(base + kNoAllocRevOffset);
+  a.counters = reinterpret_cast<uint32_t*>(base + kNoAllocCountOffset);
+  a.partials = reinterpret_cast<float*>(base + kNoAllocPartOffset);
+  a.cache_rows = (int)T;
+  a.T = (int)T;
+  a.H = H;
+  a.N = N;
+  a.Nq = Nq;
+  a.Nkv = Nkv;
+  a.d = d;
+  a.eps = (float)desc->eps;
+  a.bf16 = bf16;
+  hipError_t e = hipSuccess;
+  if (variant == QKV_VARIANT_DECODE) {
+    const int64_t elem = 2;
+    for (int64_t t0 = 0; t0 < T && e == hipSuccess; t0 += qkv::kDecodeTokens) {
+      qkv::ForwardArgs c = a;
+      c.T = (int)std::min<int64_t>(qkv::kDecodeTokens, T - t0);
+      c.x = static_cast<const char*>(x) + t0 * H * elem;
+      c.pos = pos + t0;
+      c.q = static_cast<char*>(q) + t0 * Nq * elem;
+      c.k = static_cast<char*>(k) + t0 * Nkv * elem;
+      c.v = static_cast<char*>(v) + t0 * Nkv * elem;
+      c.cache_rows = c.T;
+      e = qkv::launch_decode(c, s);
+    }
+  } else if (variant == QKV_VARIANT_PREFILL) {
+    // one launch: the plans' plain prefill kernel where the shape allows it, else the
+    // 256 x 256 kernel's normalise-on-load form (no split-K scratch, no pre-pass)
+    e = qkv::prefill_wide_supports(H, N, Nq, Nkv, d) ? qkv::launch_prefill_wide(a, s) : qkv::launch_prefill(a, s);
+  } else {
+    e = qkv::launch_generic(a, s);
+  }
+  return e == hipSuccess ? QKV_OK : QKV_ERR_HIP;
 }
 
 qkv_status qkv_rms_inv(qkv_plan plan, int64_t num_tokens, const void* x, float* inv_rms, void* stream) {
