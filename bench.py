@@ -548,6 +548,9 @@ def main() -> int:
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cache-flushed per-call prefill timing (so a profiled run holds only the "
                          "timed back-to-back forwards)")
+    ap.add_argument("--prefill-prepass", action="store_true",
+                    help="time the opt-in two-launch prefill form (QKV_PLAN_PREFILL_PREPASS) as the step "
+                         "instead of the single launch, e.g. to profile the pair")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (steps times), to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings against a known byte count")
@@ -577,8 +580,9 @@ def main() -> int:
         wl = wl.with_tokens(1, args.tokens)
     inp = workloads.make_inputs(wl)
     bufs = device_inputs(wl, inp)
-    plan = qkv.Plan.for_workload(wl)
+    plan = qkv.Plan.for_workload(wl, prefill_prepass=args.prefill_prepass)
     variant = plan.variant(wl.tokens)
+    prepass_form = args.prefill_prepass and variant == "prefill"
     print(f"[bench] {wl.name}: T={wl.tokens} H={wl.hidden} N={wl.n_total} variant={variant} "
           f"steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
     wall, kernel_s = time_forward(plan, bufs, args.steps, args.warmup)
@@ -593,7 +597,7 @@ def main() -> int:
     if not args.no_extra and wl.tokens > 256 and wl.dtype == "bf16":
         zero_s = zero_weight_leg(plan, bufs)
     plan.close()
-    if not args.no_extra and variant == "prefill":
+    if not args.no_extra and variant == "prefill" and not prepass_form:
         prepass_s = prepass_leg(qkv, wl, bufs)
 
     flops = wl.flops()
@@ -603,9 +607,10 @@ def main() -> int:
     else:
         peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
         bound, achieved, unit = "mfma", flops / kernel_s / 1e12, "TFLOP/s"
-    traffic = measured_traffic(wl.name)
+    traffic = measured_traffic(wl.name + ("+prepass" if prepass_form else ""))
     # the launches of one forward, all inside the HIP-event window that gives kernel_us
-    kernels = {"prefill": "prefill_wide_kernel (one launch, normalise-on-load)",
+    kernels = {"prefill": ("prenorm_kernel + prefill_kernel (opt-in pre-pass form)" if prepass_form else
+                           "prefill_wide_kernel (one launch, normalise-on-load)"),
                "prefill_split": "prefill_kernel (split-K form)",
                "decode": "decode_kernel", "generic": "generic kernel"}.get(variant, variant)
     out = {
@@ -624,7 +629,7 @@ def main() -> int:
         "config": {"workload": wl.name, "tokens": wl.tokens, "batch": wl.batch, "seq_len": wl.seq,
                    "hidden": wl.hidden, "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "bias": wl.has_bias, "rope_theta": wl.rope_theta, "eps": wl.eps,
-                   "variant": variant},
+                   "variant": variant, "prefill_prepass": prepass_form},
         "tflops": round(flops / kernel_s / 1e12, 2),
         "mfma_frac": round(flops / kernel_s / 1e12 / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
@@ -678,7 +683,7 @@ def main() -> int:
     torch.cuda.empty_cache()
     if not args.no_extra:
         print("[bench] configurations leg (GPU, oracle, parity)", file=sys.stderr, flush=True)
-        head = None if head_out is None else (wl.name, kernel_s, head_out, variant)
+        head = None if head_out is None or prepass_form else (wl.name, kernel_s, head_out, variant)
         out["configs"] = configs_leg(qkv, workloads, headline=head, oracle=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline leg", file=sys.stderr, flush=True)
