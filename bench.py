@@ -271,7 +271,8 @@ def decode_leg(qkv, workloads, replays: int = 125, copies: int = 8):
 
 def backward_leg(qkv, workloads, wl, bufs, steps: int = 10, warmup: int = 2):
     """The backward of the chain on the workload's shape: unrotate, recomputed
-    activations, two GEMMs (rocBLAS), norm gradient and column sums."""
+    activations, the two GEMMs (this library's MFMA kernel), norm gradient and column
+    sums."""
     import torch
     x, w, W, b, pos, q, k, v = bufs
     g = workloads.make_grads(wl)
@@ -292,8 +293,8 @@ def backward_leg(qkv, workloads, wl, bufs, steps: int = 10, warmup: int = 2):
     gemm_flops = 2 * wl.flops()
     return {"workload": wl.name, "us": round(sec * 1e6, 2), "gemm_flops": gemm_flops,
             "tflops": round(gemm_flops / sec / 1e12, 2), "mfma_frac": round(gemm_flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "note": "dW = a^T gy and ga = gy W^T on rocBLAS; unrotate, activations, norm gradient and column "
-                    "sums in this library's kernels"}
+            "note": "dW = a^T gy and ga = gy W^T on this library's 256 x 256 MFMA GEMM; unrotate, activations, "
+                    "norm gradient and column sums in its other kernels (no vendor library)"}
 
 
 def _event_time(fn, steps: int, warmup: int) -> float:

@@ -248,17 +248,21 @@ qkv_status qkv_forward_unfused(qkv_plan plan, int64_t num_tokens,
  * dx_j = r w_j ga_j - (r^3/H) x_j sum_k ga_k w_k x_k.  The page
  * "Liger-Kernel核心技术：RollingBuffer与融合算子详解" reports backward speed-ups for its
  * fused kernels next to the forward ones (section "算子融合").
- * The two products run as rocBLAS GEMMs (bf16 or fp32 operands, fp32 accumulation);
- * the rest are this library's kernels.  Column sums are done in a fixed order, so
- * results are deterministic.
+ * Every step, the two products included, runs on this library's kernels: for bf16
+ * plans both GEMMs on the matrix cores (bf16 operands, fp32 accumulation; ga = gy W^T
+ * there when N is a multiple of 32, else on fp32 FMA tiles), for fp32 plans on fp32
+ * FMA tiles.  dW is rounded once to the plan dtype from its fp32 sum; ga stays fp32.
+ * Column sums are done in a fixed order and every GEMM element is one fixed-order
+ * sum, so results are deterministic.
  * Scratch: the first backward call through a plan allocates the plan's backward
- * scratch (about max_tokens * (N*e + H*e + 4H) bytes, e = element size) and a rocBLAS
- * handle, kept until qkv_plan_destroy; later calls allocate nothing of their own
- * (rocBLAS may keep a workspace of its own).  Forwards and backwards through one plan
- * share scratch and must not overlap in time.
+ * scratch (about max_tokens * (N*e + H*e + 4H) + 8192 H bytes, e = element size), kept until
+ * qkv_plan_destroy; later calls allocate nothing.  Forwards and backwards through one
+ * plan share scratch and must not overlap in time.
+ * Limits: num_tokens * hidden * 4 < 2^31 (the fp32 activation gradient is addressed
+ * with 32-bit byte offsets), else QKV_ERR_UNSUPPORTED.
  * Alignment: every tensor 16-byte aligned except pos (4 bytes).  num_tokens == 0 is a
  * no-op.  Argument errors return QKV_ERR_INVALID_ARG before any HIP call; failed
- * scratch allocation QKV_ERR_OUT_OF_MEMORY; launch or rocBLAS failures QKV_ERR_HIP. */
+ * scratch allocation QKV_ERR_OUT_OF_MEMORY; launch failures QKV_ERR_HIP. */
 qkv_status qkv_backward(qkv_plan plan, int64_t num_tokens,
                         const void* x, const void* w_norm, const void* w_qkv, const int32_t* pos,
                         const void* dq, const void* dk, const void* dv,

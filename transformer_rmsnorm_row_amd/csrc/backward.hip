@@ -9,7 +9,10 @@
 //   dW   = a^T gy,  ga = gy W^T                                         (GEMMs)
 //   dw   = sum over tokens of ga * x * r                                (column sum)
 //   dx_j = r w_j ga_j - (r^3 / H) x_j sum_k ga_k w_k x_k                (row kernel)
-// Column sums are two-pass (fixed chunks of tokens, then the chunks in order), so
+// gy is stored transposed, gy^T [N][Tp] with Tp = T rounded up to 32 and the pad zero:
+// both GEMMs then take one operand with k contiguous and one with k as the row index,
+// the pairing the MFMA GEMM runs fastest.  Column sums are two-pass (fixed chunks of
+// tokens, then the chunks in order) and row sums one wave per row in a fixed order, so
 // every result is deterministic.
 #include <algorithm>
 
@@ -72,73 +75,127 @@ __device__ __forceinline__ void st8(void* p, size_t i, const float (&v)[8]) {
   }
 }
 
-// One thread per (token, 8 consecutive rotation pairs of one head): 16-byte loads of
-// the u and v halves.  Used when d/2 is a multiple of 8.
+// Unrotate and transpose: block (64 tokens, 32 consecutive rotation pairs) reads the
+// pairs' two columns from dq, dk or dv (Q and K pairs turned back by -angle, V pairs
+// copied), stages them in LDS as [64 columns][64 tokens], and writes the 64 gy^T rows'
+// 64-token pieces.  Pairs enumerate features i < d/2 of every head of Q, K and V; pair u
+// is column (u / half) d + u % half and its partner is half further.  Tokens in [T, Tp)
+// are written as zeros.
 template <bool BF16>
-__global__ __launch_bounds__(256) void unrotate8_kernel(BackwardArgs b) {
-  const int half = b.d / 2, units = b.N / 16;  // 8-pair groups per token
-  const size_t total = (size_t)b.T * units;
-  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
-    const int t = (int)(e / units), g = (int)(e % units);
-    const int p0 = g * 8;                                 // first pair of the group
-    const int c = (p0 / half) * b.d + (p0 % half);        // its first column
-    const void* src;
-    int width, oc;
-    if (c < b.Nq) {
-      src = b.dq; width = b.Nq; oc = c;
-    } else if (c < b.Nq + b.Nkv) {
-      src = b.dk; width = b.Nkv; oc = c - b.Nq;
-    } else {
-      src = b.dv; width = b.Nkv; oc = c - b.Nq - b.Nkv;
-    }
-    float gu[8], gv[8];
-    ld8<BF16>(src, (size_t)t * width + oc, gu);
-    ld8<BF16>(src, (size_t)t * width + oc + half, gv);
-    if (c < b.Nq + b.Nkv) {
-      const int i0 = p0 % half;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
+__global__ __launch_bounds__(256) void unrotate_t_kernel(BackwardArgs b, int tp) {
+  __shared__ float s[64][65];
+  const int half = b.d / 2, npairs = b.N / 2;
+  const int t0 = blockIdx.x * 64, u0 = blockIdx.y * 32;
+  for (int e = threadIdx.x; e < 64 * 32; e += 256) {
+    const int t = e >> 5, j = e & 31, u = u0 + j, tt = t0 + t;
+    float y0 = 0.f, y1 = 0.f;
+    if (u < npairs && tt < b.T) {
+      const int c = (u / half) * b.d + (u % half);
+      const void* src;
+      int width, oc;
+      if (c < b.Nq) {
+        src = b.dq; width = b.Nq; oc = c;
+      } else if (c < b.Nq + b.Nkv) {
+        src = b.dk; width = b.Nkv; oc = c - b.Nq;
+      } else {
+        src = b.dv; width = b.Nkv; oc = c - b.Nq - b.Nkv;
+      }
+      const float gu = ld<BF16>(src, (size_t)tt * width + oc), gv = ld<BF16>(src, (size_t)tt * width + oc + half);
+      y0 = gu;
+      y1 = gv;
+      if (c < b.Nq + b.Nkv) {
         float cs, sn;
-        rope_cos_sin(b.pos[t], b.rev_freq[i0 + j], cs, sn);
-        const float u = gu[j], v = gv[j];
-        gu[j] = u * cs + v * sn;
-        gv[j] = v * cs - u * sn;
+        rope_cos_sin(b.pos[tt], b.rev_freq[u % half], cs, sn);
+        y0 = gu * cs + gv * sn;
+        y1 = gv * cs - gu * sn;
       }
     }
-    st8<BF16>(b.gy, (size_t)t * b.N + c, gu);
-    st8<BF16>(b.gy, (size_t)t * b.N + c + half, gv);
+    s[j][t] = y0;
+    s[32 + j][t] = y1;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int jc = e >> 6, t = e & 63, tt = t0 + t;
+    const int u = u0 + (jc & 31);
+    if (u >= npairs || tt >= tp) continue;
+    const int c = (u / half) * b.d + (u % half) + (jc >= 32 ? half : 0);
+    st<BF16>(b.gy, (size_t)c * tp + tt, s[jc][t]);
   }
 }
 
-// One thread per (token, rotation pair); pairs enumerate features i < d/2 of every
-// head of Q, K and V (V pairs are copied unrotated).
+// The same with 16-byte accesses, when d/2 is a multiple of 8: block (64 tokens, 64
+// pairs) loads 8 pairs' u and v halves per thread and item, stages [128 columns][64
+// tokens] in fp32, and stores 8-token pieces of the gy^T rows.
 template <bool BF16>
-__global__ __launch_bounds__(256) void unrotate_kernel(BackwardArgs b) {
-  const int half = b.d / 2, units = b.N / 2;
-  const size_t total = (size_t)b.T * units;
-  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
-    const int t = (int)(e / units), u = (int)(e % units);
-    const int c = (u / half) * b.d + (u % half);
-    const void* src;
-    int width, oc;
-    if (c < b.Nq) {
-      src = b.dq; width = b.Nq; oc = c;
-    } else if (c < b.Nq + b.Nkv) {
-      src = b.dk; width = b.Nkv; oc = c - b.Nq;
-    } else {
-      src = b.dv; width = b.Nkv; oc = c - b.Nq - b.Nkv;
+__global__ __launch_bounds__(256) void unrotate_t8_kernel(BackwardArgs b, int tp) {
+  __shared__ float s[128][65];
+  const int half = b.d / 2, npairs = b.N / 2;
+  const int t0 = blockIdx.x * 64, u0 = blockIdx.y * 64;
+  for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+    const int gi = e & 7, t = e >> 3, tt = t0 + t, u = u0 + 8 * gi;
+    float gu[8], gv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) gu[k] = gv[k] = 0.f;
+    if (u < npairs && tt < b.T) {
+      const int c = (u / half) * b.d + (u % half);
+      const void* src;
+      int width, oc;
+      if (c < b.Nq) {
+        src = b.dq; width = b.Nq; oc = c;
+      } else if (c < b.Nq + b.Nkv) {
+        src = b.dk; width = b.Nkv; oc = c - b.Nq;
+      } else {
+        src = b.dv; width = b.Nkv; oc = c - b.Nq - b.Nkv;
+      }
+      ld8<BF16>(src, (size_t)tt * width + oc, gu);
+      ld8<BF16>(src, (size_t)tt * width + oc + half, gv);
+      if (c < b.Nq + b.Nkv) {
+        const int i0 = u % half;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          float cs, sn;
+          rope_cos_sin(b.pos[tt], b.rev_freq[i0 + k], cs, sn);
+          const float x0 = gu[k], x1 = gv[k];
+          gu[k] = x0 * cs + x1 * sn;
+          gv[k] = x1 * cs - x0 * sn;
+        }
+      }
     }
-    const float gu = ld<BF16>(src, (size_t)t * width + oc), gv = ld<BF16>(src, (size_t)t * width + oc + half);
-    float y0 = gu, y1 = gv;
-    if (c < b.Nq + b.Nkv) {
-      float cs, sn;
-      rope_cos_sin(b.pos[t], b.rev_freq[u % half], cs, sn);
-      y0 = gu * cs + gv * sn;
-      y1 = gv * cs - gu * sn;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      s[8 * gi + k][t] = gu[k];
+      s[64 + 8 * gi + k][t] = gv[k];
     }
-    st<BF16>(b.gy, (size_t)t * b.N + c, y0);
-    st<BF16>(b.gy, (size_t)t * b.N + c + half, y1);
   }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 128 * 8; e += 256) {
+    const int lc = e >> 3, tq = e & 7, tt = t0 + 8 * tq;
+    const int u = u0 + (lc & 63);
+    if (u >= npairs || tt >= tp) continue;
+    const int c = (u / half) * b.d + (u % half) + (lc >= 64 ? half : 0);
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = s[lc][8 * tq + k];
+    st8<BF16>(b.gy, (size_t)c * tp + tt, v);
+  }
+}
+
+// db[n] = sum over tokens of gy^T[n][t]: one wave per row, lane partial sums over
+// 8-token pieces in order, then a fixed shuffle tree.
+template <bool BF16>
+__global__ __launch_bounds__(256) void rowsum_kernel(BackwardArgs b, int tp) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= b.N) return;
+  float acc = 0.f;
+  for (int t = lane * 8; t < tp; t += 512) {
+    float v[8];
+    ld8<BF16>(b.gy, (size_t)n * tp + t, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += v[j];
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) st<BF16>(b.dbias, n, acc);
 }
 
 // One wave per token: r[t] and the normalised activations a = x r w in the plan dtype.
@@ -246,9 +303,57 @@ __global__ __launch_bounds__(256) void norm_grad_kernel(BackwardArgs b) {
   }
 }
 
-// Column sums over tokens, pass 1: block (column group, token chunk) -> fp32 partial.
-// kMode 0: gy[t, c]; kMode 1: ga[t, c] * x[t, c] * r[t].
-template <bool BF16, int kMode>
+// dx as norm_grad_kernel, fused with the norm-weight gradient's column sums: each wave
+// takes `tpw` consecutive tokens in order, keeps its lane's KIT x 8 column sums of
+// ga x r in registers across them, and writes them as one row of `partial` (rows in
+// wave order; the final pass adds them in that order).
+template <bool BF16, int KIT>
+__global__ __launch_bounds__(256) void norm_grad_fused_kernel(BackwardArgs b, int tpw, int nparts) {
+  const int lane = threadIdx.x & 63;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= nparts) return;
+  float col[KIT][8];
+#pragma unroll
+  for (int m = 0; m < KIT; ++m)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) col[m][j] = 0.f;
+  for (int q = 0; q < tpw; ++q) {
+    const int t = wid * tpw + q;
+    if (t >= b.T) break;
+    const size_t row = (size_t)t * b.H;
+    float g[KIT][8], x[KIT][8];
+    float inner = 0.f;
+#pragma unroll
+    for (int m = 0; m < KIT; ++m) {
+      float w[8];
+      ld8<false>(b.ga, row + lane * 8 + 512 * m, g[m]);
+      ld8<BF16>(b.w_norm, lane * 8 + 512 * m, w);
+      ld8<BF16>(b.x, row + lane * 8 + 512 * m, x[m]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) inner = fmaf(g[m][j] * w[j], x[m][j], inner);
+    }
+    inner = wave_sum(inner);
+    const float r = b.inv_rms[t];
+    const float c2 = r * r * r / (float)b.H * inner;
+#pragma unroll
+    for (int m = 0; m < KIT; ++m) {
+      float w[8], d[8];
+      ld8<BF16>(b.w_norm, lane * 8 + 512 * m, w);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        d[j] = r * w[j] * g[m][j] - c2 * x[m][j];
+        col[m][j] = fmaf(g[m][j] * x[m][j], r, col[m][j]);
+      }
+      st8<BF16>(b.dx, row + lane * 8 + 512 * m, d);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < KIT; ++m) st8<false>(b.partial, (size_t)wid * b.H + lane * 8 + 512 * m, col[m]);
+}
+
+// Column sums over tokens, pass 1: block (column group, token chunk) -> fp32 partial
+// of ga[t, c] * x[t, c] * r[t].
+template <bool BF16>
 __global__ __launch_bounds__(256) void colsum_partial_kernel(BackwardArgs b, int ncols, int chunks) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= ncols) return;
@@ -258,10 +363,7 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(BackwardArgs b, int
   // unrolled so that the loads of several tokens are in flight; the adds keep token order
 #pragma unroll 8
   for (int t = t0; t < t1; ++t) {
-    if constexpr (kMode == 0)
-      s += ld<BF16>(b.gy, (size_t)t * ncols + c);
-    else
-      s = fmaf(b.ga[(size_t)t * ncols + c] * ld<BF16>(b.x, (size_t)t * ncols + c), b.inv_rms[t], s);
+    s = fmaf(b.ga[(size_t)t * ncols + c] * ld<BF16>(b.x, (size_t)t * ncols + c), b.inv_rms[t], s);
   }
   b.partial[(size_t)blockIdx.y * ncols + c] = s;
 }
@@ -278,25 +380,46 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float* partial,
   st<BF16>(out, c, s);
 }
 
-template <bool BF16, int kMode>
+// Final pass over many partial rows: block = 16 columns x 16 slices of the rows; each
+// thread adds its slice's rows in order, then the 16 slice sums of a column are added
+// in slice order.
+template <bool BF16>
+__global__ __launch_bounds__(256) void colsum_final16_kernel(const float* partial, void* out, int ncols, int rows) {
+  __shared__ float red[16][17];
+  const int cl = threadIdx.x & 15, sl = threadIdx.x >> 4;
+  const int c = blockIdx.x * 16 + cl;
+  const int per = (rows + 15) / 16;
+  const int r0 = sl * per, r1 = min(rows, r0 + per);
+  float s = 0.f;
+  if (c < ncols) {
+#pragma unroll 16
+    for (int j = r0; j < r1; ++j) s += partial[(size_t)j * ncols + c];
+  }
+  red[sl][cl] = s;
+  __syncthreads();
+  if (sl == 0 && c < ncols) {
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v += red[k][cl];
+    st<BF16>(out, c, v);
+  }
+}
+
+template <bool BF16>
 hipError_t colsum(const BackwardArgs& b, int ncols, void* out, hipStream_t stream) {
   const int chunks = backward_colsum_chunks(b.T);
-  colsum_partial_kernel<BF16, kMode><<<dim3((ncols + 255) / 256, chunks), dim3(256), 0, stream>>>(b, ncols, chunks);
+  colsum_partial_kernel<BF16><<<dim3((ncols + 255) / 256, chunks), dim3(256), 0, stream>>>(b, ncols, chunks);
   colsum_final_kernel<BF16><<<dim3((ncols + 255) / 256), dim3(256), 0, stream>>>(b.partial, out, ncols, chunks);
   return hipGetLastError();
 }
 
 template <bool BF16>
 hipError_t pre_gemm(const BackwardArgs& b, hipStream_t stream) {
-  if ((b.d / 2) % 8 == 0) {
-    const size_t total = (size_t)b.T * (b.N / 16);
-    const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
-    unrotate8_kernel<BF16><<<dim3(blocks), dim3(256), 0, stream>>>(b);
-  } else {
-    const size_t total = (size_t)b.T * (b.N / 2);
-    const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
-    unrotate_kernel<BF16><<<dim3(blocks), dim3(256), 0, stream>>>(b);
-  }
+  const int tp = backward_token_pitch(b.T);
+  if ((b.d / 2) % 8 == 0)
+    unrotate_t8_kernel<BF16><<<dim3((tp + 63) / 64, (b.N / 2 + 63) / 64), dim3(256), 0, stream>>>(b, tp);
+  else
+    unrotate_t_kernel<BF16><<<dim3((tp + 63) / 64, (b.N / 2 + 31) / 32), dim3(256), 0, stream>>>(b, tp);
   const dim3 rows((b.T + 3) / 4), threads(256);
   switch (b.H) {
     case 1024: activations_kernel<BF16, 2><<<rows, threads, 0, stream>>>(b); break;
@@ -304,20 +427,29 @@ hipError_t pre_gemm(const BackwardArgs& b, hipStream_t stream) {
     case 4096: activations_kernel<BF16, 8><<<rows, threads, 0, stream>>>(b); break;
     default: activations_kernel<BF16, 0><<<rows, threads, 0, stream>>>(b); break;
   }
-  if (b.dbias) return colsum<BF16, 0>(b, b.N, b.dbias, stream);
+  if (b.dbias) rowsum_kernel<BF16><<<dim3((b.N + 3) / 4), dim3(256), 0, stream>>>(b, tp);
+  return hipGetLastError();
+}
+
+template <bool BF16, int KIT>
+hipError_t fused_post(const BackwardArgs& b, hipStream_t stream) {
+  const int tpw = (b.T + kBackwardPartials - 1) / kBackwardPartials;
+  const int nparts = (b.T + tpw - 1) / tpw;
+  norm_grad_fused_kernel<BF16, KIT><<<dim3((nparts + 3) / 4), dim3(256), 0, stream>>>(b, tpw, nparts);
+  colsum_final16_kernel<BF16><<<dim3((b.H + 15) / 16), dim3(256), 0, stream>>>(b.partial, b.dw_norm, b.H, nparts);
   return hipGetLastError();
 }
 
 template <bool BF16>
 hipError_t post_gemm(const BackwardArgs& b, hipStream_t stream) {
-  const dim3 rows((b.T + 3) / 4), threads(256);
   switch (b.H) {
-    case 1024: norm_grad_kernel<BF16, 2><<<rows, threads, 0, stream>>>(b); break;
-    case 2048: norm_grad_kernel<BF16, 4><<<rows, threads, 0, stream>>>(b); break;
-    case 4096: norm_grad_kernel<BF16, 8><<<rows, threads, 0, stream>>>(b); break;
-    default: norm_grad_kernel<BF16, 0><<<rows, threads, 0, stream>>>(b); break;
+    case 1024: return fused_post<BF16, 2>(b, stream);
+    case 2048: return fused_post<BF16, 4>(b, stream);
+    case 4096: return fused_post<BF16, 8>(b, stream);
+    default: break;
   }
-  return colsum<BF16, 1>(b, b.H, b.dw_norm, stream);
+  norm_grad_kernel<BF16, 0><<<dim3((b.T + 3) / 4), dim3(256), 0, stream>>>(b);
+  return colsum<BF16>(b, b.H, b.dw_norm, stream);
 }
 
 }  // namespace

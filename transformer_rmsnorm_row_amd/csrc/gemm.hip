@@ -1,0 +1,460 @@
+// The two plain GEMMs of the backward (dW = a^T gy and ga = gy W^T) on the matrix cores
+// of gfx950, and a plain fp32-FMA GEMM for fp32 plans and shapes outside the MFMA form.
+//
+// The backward of the fused chain (the page "Liger-Kernel底层优化：新一代内核级推理加速
+// 引擎介绍", fused-kernel list, "Fused RMSNorm + QKV Projection + RoPE", differentiated
+// by the chain rule) needs the weight gradient dW = a^T gy over the tokens and the
+// activation gradient ga = gy W^T over the projection's columns, with a the normalised
+// activations and gy the unrotated upstream gradient.
+//
+// MFMA form (bf16 operands, fp32 accumulation):
+//   * 256 x 256 output tile per 512-thread workgroup (8 waves, two per SIMD); wave
+//     (g, s) owns rows 128g..+127 and columns 64s..+63: 4 x 2 accumulators of
+//     v_mfma_f32_32x32x16_bf16 (128 fp32 per lane).
+//   * Each operand is one of two layouts in memory:
+//       kRowK  [rows][K], k contiguous: a step of 32 k is 64 bytes of each of the tile's
+//              256 rows, staged as [256][64 B] with the 16-byte chunks XOR-ed by bits
+//              2..3 of the row, read as fragments with ds_read_b128;
+//       kKRow  [K][cols], cols contiguous: a step is 32 rows of 512 bytes, staged as
+//              loaded with chunk c of k row r at c ^ 4 (r mod 4), read as fragments with
+//              the transpose read ds_read_b64_tr_b16.
+//     Both GEMMs take A as kKRow and B as kRowK, the pairing measured fastest (one
+//     operand of each kind: 623-633 us on 8192 x 4096 x 12288, against 650 us with both
+//     kKRow and 838 us with both kRowK): dW takes a [T, H] and gy^T [N, Tp], ga takes
+//     gy^T and W [H, N].  The unrotated gradient is written transposed for this.
+//   * Both operands go global -> LDS by DMA (buffer_load ... lds), three steps ahead
+//     into 4-deep rings (2 x 64 KB), 1 KB per instruction, two instructions per
+//     operand, wave and step.
+//   * Ping-pong: waves 0-3 and 4-7 are one phase apart.  A memory phase reads the
+//     wave's fragments of step t, issues step t + 3 and waits until its own part of
+//     step t + 1 has landed; a compute phase runs the step's 16 MFMAs.  Barriers
+//     separate the phases, so on every SIMD one wave feeds the matrix pipe while the
+//     other reads LDS.
+//   * Tails: loads outside an operand's buffer read zeros (K past the end for kKRow,
+//     rows past the end for kRowK); kRowK steps that start at or past K are sent outside
+//     the buffer, and a kRowK operand whose K is not a multiple of 32 must carry zeros
+//     in its rows from K to the next multiple of 32 (its last step reads them); stores
+//     outside the M x N result are dropped.
+//   * Tiles are numbered XCD-contiguously in groups of 4 row panels, so the ~32
+//     workgroups resident on one XCD share their operand steps in its L2.
+//   * Epilogue: each wave stages its 128 x 64 results through LDS and stores 16-byte
+//     row pieces (whole 128-byte lines), fp32 or rounded once to bf16.
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace qkv {
+
+namespace {
+
+constexpr int GM = 256, GN = 256, GK = 32;
+constexpr int kGThreads = 512;
+constexpr int kGStep = 256 * GK * 2;  // bytes of one operand's step: [256][32] or [32][256] bf16
+constexpr int kGStages = 4;
+constexpr int kGABase = 0;
+constexpr int kGBBase = kGStages * kGStep;
+constexpr int kGLds = 2 * kGStages * kGStep;  // 128 KB
+constexpr int kGGroupM = 4;
+constexpr uint32_t kOutside = 0x80000000u;  // a byte offset past every operand (all are < 2^31 bytes)
+
+constexpr int kRowK = 0, kKRow = 1;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int N>
+__device__ __forceinline__ void gwait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// [256][64 B] staging of a kRowK step: chunk c of row r at c ^ ((r >> 2) & 3)
+__device__ __forceinline__ uint32_t rowk_off(uint32_t row, uint32_t chunk) {
+  return row * 64u + ((chunk ^ ((row >> 2) & 3u)) << 4);
+}
+// [32][512 B] staging of a kKRow step: chunk c of k row r at c ^ 4 (r mod 4)
+__device__ __forceinline__ uint32_t krow_chunk(uint32_t k, uint32_t c) { return c ^ ((k & 3u) << 2); }
+
+// One operand of the MFMA GEMM: its DMA offsets and fragment reads.  `org` is the
+// tile's first row (kRowK) or column (kKRow) of this operand, `ld` its row pitch in
+// elements, `len` the rows (kRowK) or K (kKRow) the buffer holds.
+template <int kLayout>
+struct Operand {
+  u32x4 rsrc;
+  uint32_t voff[2];   // per DMA instruction, for k = 0
+  uint32_t ld2;       // row pitch in bytes
+  uint32_t kbytes;    // kRowK: K in bytes (steps at or past it are sent outside the buffer)
+
+  __device__ void init(const void* p, int org, int ld, int len, int K, int wave, int lane) {
+    const uint64_t base = reinterpret_cast<uint64_t>(p);
+    rsrc = u32x4{(uint32_t)base, (uint32_t)(base >> 32), (uint32_t)len * (uint32_t)ld * 2u, (uint32_t)kBufferWord3};
+    ld2 = (uint32_t)ld * 2u;
+    kbytes = (uint32_t)K * 2u;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if constexpr (kLayout == kRowK) {
+        // instruction i of wave w fills rows 32w + 16i .. +15; lane l physical chunk l % 4
+        // of row 32w + 16i + l / 4
+        const uint32_t r = 32u * wave + 16u * i + (lane >> 2);
+        const uint32_t c = ((uint32_t)lane & 3u) ^ ((r >> 2) & 3u);
+        voff[i] = ((uint32_t)org + r) * ld2 + c * 16u;
+      } else {
+        // instruction i of wave w fills k rows 4w + 2i, +1; lane l physical chunk l % 32
+        // of row 4w + 2i + l / 32
+        const uint32_t k = 4u * wave + 2u * i + (lane >> 5);
+        const uint32_t c = krow_chunk(k, (uint32_t)lane & 31u);
+        voff[i] = k * ld2 + ((uint32_t)org + 8u * c) * 2u;
+      }
+    }
+  }
+
+  // DMA of step t into ring slot `stage` at LDS byte `lds_base` (wave-uniform parts in
+  // scalar registers; the whole per-lane offset in the vector operand so the buffer's
+  // range check sees all of it)
+  __device__ __forceinline__ void issue(int t, int stage, uint32_t lds_base, int wave) {
+    const uint32_t k0 = (uint32_t)t * GK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      uint32_t dst, off;
+      if constexpr (kLayout == kRowK) {
+        dst = lds_base + (uint32_t)stage * kGStep + (32u * wave + 16u * i) * 64u;
+        off = k0 * 2u < kbytes ? voff[i] + k0 * 2u : kOutside;
+      } else {
+        dst = lds_base + (uint32_t)stage * kGStep + (4u * wave + 2u * i) * 512u;
+        off = voff[i] + k0 * ld2;
+      }
+      dst = __builtin_amdgcn_readfirstlane(dst);
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(off), "s"(rsrc)
+                   : "m0");
+    }
+  }
+};
+
+// Fragment of a 32-wide block (rows or columns blk..blk+31 of the operand's 256) for
+// k sub-step ks (k 16 ks .. +15 of the step): lane l gets index blk + l % 32, k 8 (l / 32)
+// .. +7, the operand layout of v_mfma_f32_32x32x16_bf16 for A rows and B columns alike.
+template <int kLayout>
+__device__ __forceinline__ bf16x8 read_frag(const uint8_t* stage_base, uint32_t blk, int ks, int lane) {
+  if constexpr (kLayout == kRowK) {
+    const uint32_t row = blk + ((uint32_t)lane & 31u), chunk = 2u * ks + ((uint32_t)lane >> 5);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage_base + rowk_off(row, chunk)));
+  } else {
+    // transpose reads: 16-lane group g covers k rows 8 (g / 2) + 0..3 (+4 for the second
+    // read) and indices 16 (g % 2) + 0..15 of the block; lane j of the group points at
+    // k row j / 4, indices 4 (j % 4) .. +3
+    const uint32_t tg = (uint32_t)lane >> 4, tj = (uint32_t)lane & 15u;
+    const uint32_t k = 16u * ks + 8u * (tg >> 1) + (tj >> 2);
+    const uint32_t col = blk + 16u * (tg & 1u) + 4u * (tj & 3u);
+    const uint8_t* p = stage_base + k * 512u + krow_chunk(k, col >> 3) * 16u + (col & 7u) * 2u;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
+template <int N>
+using GInt = std::integral_constant<int, N>;
+
+template <int kLA, int kLB, bool kOutF32>
+__global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int nk) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kGLds];
+
+  // ---- tile: XCD-contiguous numbering, then groups of kGGroupM row panels
+  const int G = tiles_m * tiles_n;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int q8 = G >> 3, r8 = G & 7;
+  const int L = (xcd < r8) ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
+  const int group = L / (kGGroupM * tiles_n);
+  const int first_m = group * kGGroupM;
+  const int gm = min(tiles_m - first_m, kGGroupM);
+  const int idx = L - group * kGGroupM * tiles_n;
+  const int m0 = (first_m + idx % gm) * GM, n0 = (idx / gm) * GN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, slot = wave & 3;
+
+  Operand<kLA> opa;
+  Operand<kLB> opb;
+  // A: rows m of the result; kRowK holds them as rows of length K, kKRow as columns
+  opa.init(g.a, m0, g.lda, kLA == kRowK ? g.M : g.K, g.K, wave, lane);
+  opb.init(g.b, n0, g.ldb, kLB == kRowK ? g.N : g.K, g.K, wave, lane);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  bf16x8 fa[4][2], fb[2][2];
+  auto read_frags = [&](int stage) {
+    const uint8_t* sa = smem + kGABase + stage * kGStep;
+    const uint8_t* sb = smem + kGBBase + stage * kGStep;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) fa[rb][ks] = read_frag<kLA>(sa, 128u * grp + 32u * rb, ks, lane);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) fb[cb][ks] = read_frag<kLB>(sb, 64u * slot + 32u * cb, ks, lane);
+    }
+  };
+  auto issue = [&](int t, int stage) {
+    opa.issue(t, stage, lds0 + kGABase, wave);
+    opb.issue(t, stage, lds0 + kGBBase, wave);
+  };
+  constexpr int kOps = 4;  // vector-memory instructions per wave and step
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // end of a memory phase: this wave's fragment reads have returned (the other group
+  // issues DMA into the ring slot this wave read one step earlier right after it),
+  // while its DMA stays in flight
+  auto raw_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Step t (t % 4 == P).  Memory phase: fragments of step t from slot P; issue step
+  // t + 3 into slot (t + 3) % 4, which held step t - 1: this group read it in its
+  // previous memory phase and the other group in the memory phase that ended at the
+  // last barrier.  Per wave the DMA order is ..., t + 1, t + 2, t + 3, so this wave's
+  // part of step t + 1 has landed once at most 2 kOps instructions are outstanding, and
+  // every wave's part has before the barrier after which step t + 1 is first read.
+  // Mode: 0 issue t + 3; 1 nothing to issue (t = nk - 3); 2 wait for the last step
+  // (t = nk - 2); 3 the last step.
+  auto step = [&](auto Pc, int t, auto ModeC) {
+    constexpr int P = decltype(Pc)::value;
+    constexpr int kMode = decltype(ModeC)::value;
+    read_frags(P);
+    if constexpr (kMode == 0) {
+      issue(t + 3, (P + 3) & 3);
+      gwait_vmcnt<2 * kOps>();
+    } else if constexpr (kMode == 1) {
+      gwait_vmcnt<kOps>();
+    } else if constexpr (kMode == 2) {
+      gwait_vmcnt<0>();
+    }
+    raw_barrier();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ks = i >> 3, rb = (i >> 1) & 3, cb = i & 1;
+      acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[rb][ks], fb[cb][ks], acc[rb][cb], 0, 0, 0);
+    }
+    barrier();
+  };
+
+  // prologue: steps 0..2 issued, this wave's part of step 0 landed
+#pragma unroll
+  for (int s = 0; s < 3; ++s) issue(s, s);
+  gwait_vmcnt<2 * kOps>();
+  barrier();
+  // waves 4-7 start one phase late
+  if (grp == 1) barrier();
+  int t = 0;
+  for (; t < nk - 4; t += 4) {
+    step(GInt<0>{}, t, GInt<0>{});
+    step(GInt<1>{}, t + 1, GInt<0>{});
+    step(GInt<2>{}, t + 2, GInt<0>{});
+    step(GInt<3>{}, t + 3, GInt<0>{});
+  }
+  step(GInt<0>{}, t, GInt<0>{});
+  step(GInt<1>{}, t + 1, GInt<1>{});
+  step(GInt<2>{}, t + 2, GInt<2>{});
+  step(GInt<3>{}, t + 3, GInt<3>{});
+  if (grp == 0) barrier();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue through LDS: the rings are free (every wave's last fragment reads
+  // returned before the last barrier).  Accumulator register r of lane l is row
+  // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of its 32 x 32 block.  Each wave stages
+  // its results in a private 16 KB region, column bit 5 flipped on rows with bit 2 set
+  // (lanes 32-63 write the row 4 below lanes 0-31 and so land on the other banks), reads
+  // them back as 16-byte row pieces and stores those: whole 128-byte lines.
+  uint8_t* ws = smem + wave * 16384;
+  const uint32_t swz = (((uint32_t)lane >> 5) & 1u) << 5;  // (row >> 2) & 1 of every row this lane writes
+  const auto c_rsrc = make_rsrc(g.c, (uint32_t)g.M * (uint32_t)g.ldc * (kOutF32 ? 4u : 2u));
+  if constexpr (kOutF32) {
+    // two passes of 64 rows x 64 fp32 columns (256-byte rows)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t row = 32u * rh + 8u * (r >> 2) + 4u * ((uint32_t)lane >> 5) + (r & 3);
+            const uint32_t col = (32u * cb + ((uint32_t)lane & 31u)) ^ swz;
+            const float v = acc[2 * p + rh][cb][r];
+            *reinterpret_cast<float*>(ws + row * 256u + col * 4u) = v;
+          }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t row = 4u * j + ((uint32_t)lane >> 4), q = (uint32_t)lane & 15u;
+        const uint32_t pc = (4u * q) ^ (((row >> 2) & 1u) << 5);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ws + row * 256u + pc * 4u);
+        const int grow = m0 + 128 * grp + 64 * p + (int)row, gcol = n0 + 64 * slot + 4 * (int)q;
+        // rows past M fall outside the buffer's range; columns past N are sent outside it
+        const uint32_t off = gcol < g.N ? ((uint32_t)grow * (uint32_t)g.ldc + (uint32_t)gcol) * 4u : kOutside;
+        buf_store16(v, c_rsrc, off);
+      }
+    }
+  } else {
+    // one pass: 128 rows x 64 bf16 columns (128-byte rows)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t row = 32u * rb + 8u * (r >> 2) + 4u * ((uint32_t)lane >> 5) + (r & 3);
+          const uint32_t col = (32u * cb + ((uint32_t)lane & 31u)) ^ swz;
+          const float v = acc[rb][cb][r];
+          *reinterpret_cast<uint16_t*>(ws + row * 128u + col * 2u) = f32_to_bf16(v);
+        }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t row = 8u * j + ((uint32_t)lane >> 3), q = (uint32_t)lane & 7u;
+      const uint32_t pc = (8u * q) ^ (((row >> 2) & 1u) << 5);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ws + row * 128u + pc * 2u);
+      const int grow = m0 + 128 * grp + (int)row, gcol = n0 + 64 * slot + 8 * (int)q;
+      const uint32_t off = gcol < g.N ? ((uint32_t)grow * (uint32_t)g.ldc + (uint32_t)gcol) * 2u : kOutside;
+      buf_store16(v, c_rsrc, off);
+    }
+  }
+}
+
+// ---- plain FMA GEMM: 64 x 64 tile per 256-thread block, 4 x 4 results per thread,
+// K in chunks of 16 staged in LDS as fp32.
+template <bool BF16>
+__device__ __forceinline__ float gload(const void* p, size_t i) {
+  if constexpr (BF16)
+    return bf16_to_f32(((const uint16_t*)p)[i]);
+  else
+    return ((const float*)p)[i];
+}
+
+template <int kLA, int kLB, bool BF16, bool kOutF32>
+__global__ __launch_bounds__(256) void gemm_fma_kernel(GemmArgs g) {
+  __shared__ float sa[16][64 + 4];
+  __shared__ float sb[16][64 + 4];
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, tm = tid >> 4, tn = tid & 15;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < g.K; k0 += 16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = tid + 256 * e;  // 1024 elements of each 64 x 16 tile
+      const int kk = i & 15, mm = i >> 4;
+      const int k = k0 + kk;
+      const int m = m0 + mm, n = n0 + mm;
+      float va = 0.f, vb = 0.f;
+      if (k < g.K && m < g.M)
+        va = gload<BF16>(g.a, kLA == kRowK ? (size_t)m * g.lda + k : (size_t)k * g.lda + m);
+      if (k < g.K && n < g.N)
+        vb = gload<BF16>(g.b, kLB == kRowK ? (size_t)n * g.ldb + k : (size_t)k * g.ldb + n);
+      sa[kk][mm] = va;
+      sb[kk][mm] = vb;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = sa[kk][tm + 16 * i];
+        bv[i] = sb[kk][tn + 16 * i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + tm + 16 * i, n = n0 + tn + 16 * j;
+      if (m < g.M && n < g.N) {
+        if constexpr (kOutF32)
+          ((float*)g.c)[(size_t)m * g.ldc + n] = acc[i][j];
+        else if constexpr (BF16)
+          ((uint16_t*)g.c)[(size_t)m * g.ldc + n] = f32_to_bf16(acc[i][j]);
+        else
+          ((float*)g.c)[(size_t)m * g.ldc + n] = acc[i][j];
+      }
+    }
+}
+
+template <int kLA, int kLB, bool kOutF32>
+hipError_t run_mfma(const GemmArgs& g, hipStream_t s) {
+  const int tiles_m = (g.M + GM - 1) / GM, tiles_n = (g.N + GN - 1) / GN;
+  const int nk = ((g.K + GK - 1) / GK + 3) / 4 * 4;  // whole groups of 4 steps; the extra read zeros
+  gemm_mfma_kernel<kLA, kLB, kOutF32><<<dim3(tiles_m * tiles_n), dim3(kGThreads), 0, s>>>(g, tiles_m, tiles_n, nk);
+  return hipGetLastError();
+}
+
+template <int kLA, int kLB, bool kOutF32>
+hipError_t run_fma(const GemmArgs& g, bool bf16, hipStream_t s) {
+  const dim3 grid((g.N + 63) / 64, (g.M + 63) / 64), block(256);
+  if (bf16)
+    gemm_fma_kernel<kLA, kLB, true, kOutF32><<<grid, block, 0, s>>>(g);
+  else
+    gemm_fma_kernel<kLA, kLB, false, kOutF32><<<grid, block, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_gemms(const BackwardArgs& b, void* dw, hipStream_t s) {
+  const int tp = backward_token_pitch(b.T);
+  // dW [H, N] (plan dtype) = a^T gy: M = H, N = N, K = T; a [T, H] is [K][cols] and its
+  // buffer range ends at row T (the last step's rows past it read zeros), gy^T [N, Tp] is
+  // [rows][K] with a zero pad from T to Tp (the last step reads it in whole 32-wide k
+  // pieces)
+  GemmArgs w{};
+  w.a = b.act;
+  w.b = b.gy;
+  w.c = dw;
+  w.M = b.H;
+  w.N = b.N;
+  w.K = b.T;
+  w.lda = b.H;
+  w.ldb = tp;
+  w.ldc = b.N;
+  // ga [T, H] (fp32) = gy W^T: M = T, N = H, K = N; gy^T [N, Tp] is [K][cols], W [H, N]
+  // is [rows][K]
+  GemmArgs a{};
+  a.a = b.gy;
+  a.b = b.w;
+  a.c = b.ga;
+  a.M = b.T;
+  a.N = b.H;
+  a.K = b.N;
+  a.lda = tp;
+  a.ldb = b.N;
+  a.ldc = b.H;
+  hipError_t e;
+  if (b.bf16) {
+    e = run_mfma<kKRow, kRowK, false>(w, s);
+    if (e != hipSuccess) return e;
+    // W's rows are read in whole 32-wide k steps
+    if (b.N % GK == 0) return run_mfma<kKRow, kRowK, true>(a, s);
+    return run_fma<kKRow, kRowK, true>(a, true, s);
+  }
+  e = run_fma<kKRow, kRowK, false>(w, false, s);
+  if (e != hipSuccess) return e;
+  return run_fma<kKRow, kRowK, true>(a, false, s);
+}
+
+}  // namespace qkv

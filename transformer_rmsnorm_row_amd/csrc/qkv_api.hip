@@ -43,8 +43,8 @@ struct Plan {
   void* bwd_gy;         // [max_tokens, N] plan dtype
   void* bwd_act;        // [max_tokens, H] plan dtype
   float* bwd_ga;        // [max_tokens, H] fp32
-  float* bwd_partial;   // [kBackwardChunks, max(N, H)] fp32
-  rocblas_handle blas;  // the two GEMMs of the backward, the unfused forward's GEMM
+  float* bwd_partial;   // [kBackwardPartials, H] fp32
+  rocblas_handle blas;  // the unfused forward's GEMM (created on its first call)
 };
 
 std::mutex g_mu;
@@ -132,23 +132,23 @@ qkv_status ensure_blas(Plan* pl) {
   return ensure_blas_locked(pl);
 }
 
-// First backward through a plan: its scratch and the GEMM library handle.
+// First backward through a plan: its scratch.
 qkv_status ensure_backward_scratch(Plan* pl) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (pl->bwd_partial) return ensure_blas_locked(pl);
+  if (pl->bwd_partial) return QKV_OK;
   const size_t T = (size_t)pl->desc.max_tokens, H = (size_t)pl->desc.hidden, N = (size_t)pl->N;
   const size_t elem = pl->bf16 ? 2 : 4;
-  const size_t widest = N > H ? N : H;
   // each buffer is allocated once: a call after a failed allocation keeps what succeeded
-  bool ok = (pl->bwd_gy || hipMalloc(&pl->bwd_gy, T * N * elem) == hipSuccess) &&
+  const size_t tp = (size_t)qkv::backward_token_pitch((int)T);
+  bool ok = (pl->bwd_gy || hipMalloc(&pl->bwd_gy, tp * N * elem) == hipSuccess) &&
             (pl->bwd_act || hipMalloc(&pl->bwd_act, T * H * elem) == hipSuccess) &&
             (pl->bwd_ga || hipMalloc(&pl->bwd_ga, T * H * sizeof(float)) == hipSuccess) &&
-            hipMalloc(&pl->bwd_partial, (size_t)qkv::kBackwardChunks * widest * sizeof(float)) == hipSuccess;
+            hipMalloc(&pl->bwd_partial, (size_t)qkv::kBackwardPartials * H * sizeof(float)) == hipSuccess;
   if (!ok) {
     (void)hipGetLastError();
     return QKV_ERR_OUT_OF_MEMORY;
   }
-  return ensure_blas_locked(pl);
+  return QKV_OK;
 }
 
 // Token counts the decode kernel takes, run over consecutive chunks of kDecodeTokens.
@@ -665,6 +665,11 @@ qkv_status qkv_backward(qkv_plan plan, int64_t num_tokens, const void* x, const 
   for (const void* p : {x, w_norm, w_qkv, dq, dk, dv, (const void*)dx, (const void*)dw_norm, (const void*)dw_qkv})
     if (!aligned(p, 16)) return QKV_ERR_INVALID_ARG;
   if (!aligned(pos, 4) || (dbias && !aligned(dbias, 16))) return QKV_ERR_INVALID_ARG;
+  // the fp32 activation gradient [T, H] is addressed with 32-bit byte offsets too
+  if (num_tokens * pl->desc.hidden * 4 >= kMaxBytes) return QKV_ERR_UNSUPPORTED;
+  // and so is the transposed gradient [N, T rounded up to 32]
+  if ((int64_t)qkv::backward_token_pitch((int)num_tokens) * pl->N * (pl->bf16 ? 2 : 4) >= kMaxBytes)
+    return QKV_ERR_UNSUPPORTED;
   qkv_status st = check_device(pl);
   if (st != QKV_OK) return st;
   st = ensure_backward_scratch(pl);
@@ -674,6 +679,7 @@ qkv_status qkv_backward(qkv_plan plan, int64_t num_tokens, const void* x, const 
   qkv::BackwardArgs b{};
   b.x = x;
   b.w_norm = w_norm;
+  b.w = w_qkv;
   b.pos = pos;
   b.dq = dq;
   b.dk = dk;
@@ -697,22 +703,8 @@ qkv_status qkv_backward(qkv_plan plan, int64_t num_tokens, const void* x, const 
   b.bf16 = pl->bf16;
   if (qkv::launch_backward_pre_gemm(b, s) != hipSuccess) return QKV_ERR_HIP;
 
-  // Row-major [T, N] gy is the column-major N x T matrix gy^T (leading dimension N),
-  // and likewise for a, W and the outputs.
-  //   dW (row-major [H, N])  = a^T gy   <=>  (column-major N x H) = gy^T (N x T) * a (T x H)
-  //   ga (row-major [T, H])  = gy W^T   <=>  (column-major H x T) = W (H x N) * gy^T (N x T)
-  if (rocblas_set_stream(pl->blas, s) != rocblas_status_success) return QKV_ERR_HIP;
-  const rocblas_datatype io = pl->bf16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-  const float one = 1.0f, zero = 0.0f;
-  const int T = b.T, H = b.H, N = b.N;
-  rocblas_status rs = rocblas_gemm_ex(pl->blas, rocblas_operation_none, rocblas_operation_transpose, N, H, T, &one,
-                                      b.gy, io, N, b.act, io, H, &zero, dw_qkv, io, N, dw_qkv, io, N,
-                                      rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  if (rs != rocblas_status_success) return QKV_ERR_HIP;
-  rs = rocblas_gemm_ex(pl->blas, rocblas_operation_transpose, rocblas_operation_none, H, T, N, &one, w_qkv, io, N,
-                       b.gy, io, N, &zero, b.ga, rocblas_datatype_f32_r, H, b.ga, rocblas_datatype_f32_r, H,
-                       rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  if (rs != rocblas_status_success) return QKV_ERR_HIP;
+  // dW = a^T gy straight into the caller's dw_qkv, ga = gy W^T into plan scratch
+  if (qkv::launch_backward_gemms(b, dw_qkv, s) != hipSuccess) return QKV_ERR_HIP;
   return qkv::launch_backward_post_gemm(b, s) == hipSuccess ? QKV_OK : QKV_ERR_HIP;
 }
 
