@@ -251,15 +251,16 @@ qkv_status qkv_forward_unfused(qkv_plan plan, int64_t num_tokens,
  * Every step, the two products included, runs on this library's kernels: for bf16
  * plans both GEMMs on the matrix cores (bf16 operands, fp32 accumulation; ga = gy W^T
  * there when N is a multiple of 32, else on fp32 FMA tiles), for fp32 plans on fp32
- * FMA tiles.  dW is rounded once to the plan dtype from its fp32 sum; ga stays fp32.
+ * FMA tiles.  dW and the intermediate ga are rounded once to the plan dtype from their
+ * fp32 sums.
  * Column sums are done in a fixed order and every GEMM element is one fixed-order
  * sum, so results are deterministic.
  * Scratch: the first backward call through a plan allocates the plan's backward
- * scratch (about max_tokens * (N*e + H*e + 4H) + 8192 H bytes, e = element size), kept until
+ * scratch (about max_tokens * (N + 2H) * e + 8192 H bytes, e = element size), kept until
  * qkv_plan_destroy; later calls allocate nothing.  Forwards and backwards through one
  * plan share scratch and must not overlap in time.
- * Limits: num_tokens * hidden * 4 < 2^31 (the fp32 activation gradient is addressed
- * with 32-bit byte offsets), else QKV_ERR_UNSUPPORTED.
+ * Limits: ceil(num_tokens / 32) * 32 * N * e < 2^31 (the transposed upstream gradient
+ * is addressed with 32-bit byte offsets), else QKV_ERR_UNSUPPORTED.
  * Alignment: every tensor 16-byte aligned except pos (4 bytes).  num_tokens == 0 is a
  * no-op.  Argument errors return QKV_ERR_INVALID_ARG before any HIP call; failed
  * scratch allocation QKV_ERR_OUT_OF_MEMORY; launch failures QKV_ERR_HIP. */

@@ -6,7 +6,8 @@
 // inverse RMS and a = x r w the normalised activations:
 //   gy   = the rotation by -angle of each (dQ, dK) pair, dV unchanged   (unrotate)
 //   db   = sum over tokens of gy                                        (column sum)
-//   dW   = a^T gy,  ga = gy W^T                                         (GEMMs)
+//   dW   = a^T gy,  ga = gy W^T                                         (GEMMs; ga rounded
+//                                                                         once to the plan dtype)
 //   dw   = sum over tokens of ga * x * r                                (column sum)
 //   dx_j = r w_j ga_j - (r^3 / H) x_j sum_k ga_k w_k x_k                (row kernel)
 // gy is stored transposed, gy^T [N][Tp] with Tp = T rounded up to 32 and the pad zero:
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(256) void norm_grad_kernel(BackwardArgs b) {
 #pragma unroll
     for (int m = 0; m < KIT; ++m) {
       float w[8];
-      ld8<false>(b.ga, row + lane * 8 + 512 * m, g[m]);
+      ld8<BF16>(b.ga, row + lane * 8 + 512 * m, g[m]);
       ld8<BF16>(b.w_norm, lane * 8 + 512 * m, w);
       ld8<BF16>(b.x, row + lane * 8 + 512 * m, x[m]);
 #pragma unroll
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(256) void norm_grad_kernel(BackwardArgs b) {
   float inner = 0.f;
   for (int k = lane * 8; k < b.H; k += 512) {
     float g[8], w[8], x[8];
-    ld8<false>(b.ga, row + k, g);
+    ld8<BF16>(b.ga, row + k, g);
     ld8<BF16>(b.w_norm, k, w);
     ld8<BF16>(b.x, row + k, x);
 #pragma unroll
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(256) void norm_grad_kernel(BackwardArgs b) {
   const float c2 = r * r * r / (float)b.H * inner;
   for (int k = lane * 8; k < b.H; k += 512) {
     float g[8], w[8], x[8];
-    ld8<false>(b.ga, row + k, g);
+    ld8<BF16>(b.ga, row + k, g);
     ld8<BF16>(b.w_norm, k, w);
     ld8<BF16>(b.x, row + k, x);
 #pragma unroll
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(256) void norm_grad_fused_kernel(BackwardArgs b, in
 #pragma unroll
     for (int m = 0; m < KIT; ++m) {
       float w[8];
-      ld8<false>(b.ga, row + lane * 8 + 512 * m, g[m]);
+      ld8<BF16>(b.ga, row + lane * 8 + 512 * m, g[m]);
       ld8<BF16>(b.w_norm, lane * 8 + 512 * m, w);
       ld8<BF16>(b.x, row + lane * 8 + 512 * m, x[m]);
 #pragma unroll
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(BackwardArgs b, int
   // unrolled so that the loads of several tokens are in flight; the adds keep token order
 #pragma unroll 8
   for (int t = t0; t < t1; ++t) {
-    s = fmaf(b.ga[(size_t)t * ncols + c] * ld<BF16>(b.x, (size_t)t * ncols + c), b.inv_rms[t], s);
+    s = fmaf(ld<BF16>(b.ga, (size_t)t * ncols + c) * ld<BF16>(b.x, (size_t)t * ncols + c), b.inv_rms[t], s);
   }
   b.partial[(size_t)blockIdx.y * ncols + c] = s;
 }

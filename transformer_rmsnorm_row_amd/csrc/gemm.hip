@@ -21,7 +21,8 @@
 //     Both GEMMs take A as kKRow and B as kRowK, the pairing measured fastest (one
 //     operand of each kind: 623-633 us on 8192 x 4096 x 12288, against 650 us with both
 //     kKRow and 838 us with both kRowK): dW takes a [T, H] and gy^T [N, Tp], ga takes
-//     gy^T and W [H, N].  The unrotated gradient is written transposed for this.
+//     gy^T and W [H, N].  The unrotated gradient is written transposed for this.  Both
+//     results are rounded once to the plan dtype.
 //   * Both operands go global -> LDS by DMA (buffer_load ... lds), three steps ahead
 //     into 4-deep rings (2 x 64 KB), 1 KB per instruction, two instructions per
 //     operand, wave and step.
@@ -37,8 +38,8 @@
 //     outside the M x N result are dropped.
 //   * Tiles are numbered XCD-contiguously in groups of 4 row panels, so the ~32
 //     workgroups resident on one XCD share their operand steps in its L2.
-//   * Epilogue: each wave stages its 128 x 64 results through LDS and stores 16-byte
-//     row pieces (whole 128-byte lines), fp32 or rounded once to bf16.
+//   * Epilogue: each wave stages its 128 x 64 results, rounded once to bf16, through LDS
+//     and stores 16-byte row pieces (whole 128-byte lines).
 #include <type_traits>
 
 #include "device_common.h"
@@ -156,7 +157,7 @@ __device__ __forceinline__ bf16x8 read_frag(const uint8_t* stage_base, uint32_t 
 template <int N>
 using GInt = std::integral_constant<int, N>;
 
-template <int kLA, int kLB, bool kOutF32>
+template <int kLA, int kLB>
 __global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int nk) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kGLds];
 
@@ -275,65 +276,40 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int
   // ---- epilogue through LDS: the rings are free (every wave's last fragment reads
   // returned before the last barrier).  Accumulator register r of lane l is row
   // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of its 32 x 32 block.  Each wave stages
-  // its results in a private 16 KB region, column bit 5 flipped on rows with bit 2 set
-  // (lanes 32-63 write the row 4 below lanes 0-31 and so land on the other banks), reads
-  // them back as 16-byte row pieces and stores those: whole 128-byte lines.
+  // its 128 x 64 results, rounded once to bf16, in a private 16 KB region (128-byte
+  // rows), column bit 5 flipped on rows with bit 2 set (lanes 32-63 write the row 4
+  // below lanes 0-31 and so land on the other banks), reads them back as 16-byte row
+  // pieces and stores those: whole 128-byte lines.
   uint8_t* ws = smem + wave * 16384;
   const uint32_t swz = (((uint32_t)lane >> 5) & 1u) << 5;  // (row >> 2) & 1 of every row this lane writes
-  const auto c_rsrc = make_rsrc(g.c, (uint32_t)g.M * (uint32_t)g.ldc * (kOutF32 ? 4u : 2u));
-  if constexpr (kOutF32) {
-    // two passes of 64 rows x 64 fp32 columns (256-byte rows)
+  const auto c_rsrc = make_rsrc(g.c, (uint32_t)g.M * (uint32_t)g.ldc * 2u);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+  for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int rh = 0; rh < 2; ++rh)
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint32_t row = 32u * rh + 8u * (r >> 2) + 4u * ((uint32_t)lane >> 5) + (r & 3);
-            const uint32_t col = (32u * cb + ((uint32_t)lane & 31u)) ^ swz;
-            const float v = acc[2 * p + rh][cb][r];
-            *reinterpret_cast<float*>(ws + row * 256u + col * 4u) = v;
-          }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t row = 4u * j + ((uint32_t)lane >> 4), q = (uint32_t)lane & 15u;
-        const uint32_t pc = (4u * q) ^ (((row >> 2) & 1u) << 5);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(ws + row * 256u + pc * 4u);
-        const int grow = m0 + 128 * grp + 64 * p + (int)row, gcol = n0 + 64 * slot + 4 * (int)q;
-        // rows past M fall outside the buffer's range; columns past N are sent outside it
-        const uint32_t off = gcol < g.N ? ((uint32_t)grow * (uint32_t)g.ldc + (uint32_t)gcol) * 4u : kOutside;
-        buf_store16(v, c_rsrc, off);
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t row = 32u * rb + 8u * (r >> 2) + 4u * ((uint32_t)lane >> 5) + (r & 3);
+        const uint32_t col = (32u * cb + ((uint32_t)lane & 31u)) ^ swz;
+        // the element is copied out as a float first: a bit cast taken straight from the
+        // vector element stored element 0 of the accumulator for every r
+        const float v = acc[rb][cb][r];
+        *reinterpret_cast<uint16_t*>(ws + row * 128u + col * 2u) = f32_to_bf16(v);
       }
-    }
-  } else {
-    // one pass: 128 rows x 64 bf16 columns (128-byte rows)
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t row = 32u * rb + 8u * (r >> 2) + 4u * ((uint32_t)lane >> 5) + (r & 3);
-          const uint32_t col = (32u * cb + ((uint32_t)lane & 31u)) ^ swz;
-          const float v = acc[rb][cb][r];
-          *reinterpret_cast<uint16_t*>(ws + row * 128u + col * 2u) = f32_to_bf16(v);
-        }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t row = 8u * j + ((uint32_t)lane >> 3), q = (uint32_t)lane & 7u;
-      const uint32_t pc = (8u * q) ^ (((row >> 2) & 1u) << 5);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ws + row * 128u + pc * 2u);
-      const int grow = m0 + 128 * grp + (int)row, gcol = n0 + 64 * slot + 8 * (int)q;
-      const uint32_t off = gcol < g.N ? ((uint32_t)grow * (uint32_t)g.ldc + (uint32_t)gcol) * 2u : kOutside;
-      buf_store16(v, c_rsrc, off);
-    }
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t row = 8u * j + ((uint32_t)lane >> 3), q = (uint32_t)lane & 7u;
+    const uint32_t pc = (8u * q) ^ (((row >> 2) & 1u) << 5);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ws + row * 128u + pc * 2u);
+    const int grow = m0 + 128 * grp + (int)row, gcol = n0 + 64 * slot + 8 * (int)q;
+    // rows past M fall outside the buffer's range; columns past N are sent outside it
+    const uint32_t off = gcol < g.N ? ((uint32_t)grow * (uint32_t)g.ldc + (uint32_t)gcol) * 2u : kOutside;
+    buf_store16(v, c_rsrc, off);
   }
 }
 
 // ---- plain FMA GEMM: 64 x 64 tile per 256-thread block, 4 x 4 results per thread,
-// K in chunks of 16 staged in LDS as fp32.
+// K in chunks of 16 staged in LDS as fp32; results in the operands' dtype.
 template <bool BF16>
 __device__ __forceinline__ float gload(const void* p, size_t i) {
   if constexpr (BF16)
@@ -342,7 +318,7 @@ __device__ __forceinline__ float gload(const void* p, size_t i) {
     return ((const float*)p)[i];
 }
 
-template <int kLA, int kLB, bool BF16, bool kOutF32>
+template <int kLA, int kLB, bool BF16>
 __global__ __launch_bounds__(256) void gemm_fma_kernel(GemmArgs g) {
   __shared__ float sa[16][64 + 4];
   __shared__ float sb[16][64 + 4];
@@ -386,9 +362,8 @@ __global__ __launch_bounds__(256) void gemm_fma_kernel(GemmArgs g) {
     for (int j = 0; j < 4; ++j) {
       const int m = m0 + tm + 16 * i, n = n0 + tn + 16 * j;
       if (m < g.M && n < g.N) {
-        if constexpr (kOutF32)
-          ((float*)g.c)[(size_t)m * g.ldc + n] = acc[i][j];
-        else if constexpr (BF16)
+        // the operands' dtype, rounded once for bf16
+        if constexpr (BF16)
           ((uint16_t*)g.c)[(size_t)m * g.ldc + n] = f32_to_bf16(acc[i][j]);
         else
           ((float*)g.c)[(size_t)m * g.ldc + n] = acc[i][j];
@@ -396,21 +371,21 @@ __global__ __launch_bounds__(256) void gemm_fma_kernel(GemmArgs g) {
     }
 }
 
-template <int kLA, int kLB, bool kOutF32>
+template <int kLA, int kLB>
 hipError_t run_mfma(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (g.M + GM - 1) / GM, tiles_n = (g.N + GN - 1) / GN;
   const int nk = ((g.K + GK - 1) / GK + 3) / 4 * 4;  // whole groups of 4 steps; the extra read zeros
-  gemm_mfma_kernel<kLA, kLB, kOutF32><<<dim3(tiles_m * tiles_n), dim3(kGThreads), 0, s>>>(g, tiles_m, tiles_n, nk);
+  gemm_mfma_kernel<kLA, kLB><<<dim3(tiles_m * tiles_n), dim3(kGThreads), 0, s>>>(g, tiles_m, tiles_n, nk);
   return hipGetLastError();
 }
 
-template <int kLA, int kLB, bool kOutF32>
+template <int kLA, int kLB>
 hipError_t run_fma(const GemmArgs& g, bool bf16, hipStream_t s) {
   const dim3 grid((g.N + 63) / 64, (g.M + 63) / 64), block(256);
   if (bf16)
-    gemm_fma_kernel<kLA, kLB, true, kOutF32><<<grid, block, 0, s>>>(g);
+    gemm_fma_kernel<kLA, kLB, true><<<grid, block, 0, s>>>(g);
   else
-    gemm_fma_kernel<kLA, kLB, false, kOutF32><<<grid, block, 0, s>>>(g);
+    gemm_fma_kernel<kLA, kLB, false><<<grid, block, 0, s>>>(g);
   return hipGetLastError();
 }
 
@@ -432,8 +407,8 @@ hipError_t launch_backward_gemms(const BackwardArgs& b, void* dw, hipStream_t s)
   w.lda = b.H;
   w.ldb = tp;
   w.ldc = b.N;
-  // ga [T, H] (fp32) = gy W^T: M = T, N = H, K = N; gy^T [N, Tp] is [K][cols], W [H, N]
-  // is [rows][K]
+  // ga [T, H] (plan dtype) = gy W^T: M = T, N = H, K = N; gy^T [N, Tp] is [K][cols], W
+  // [H, N] is [rows][K]
   GemmArgs a{};
   a.a = b.gy;
   a.b = b.w;
@@ -446,15 +421,15 @@ hipError_t launch_backward_gemms(const BackwardArgs& b, void* dw, hipStream_t s)
   a.ldc = b.H;
   hipError_t e;
   if (b.bf16) {
-    e = run_mfma<kKRow, kRowK, false>(w, s);
+    e = run_mfma<kKRow, kRowK>(w, s);
     if (e != hipSuccess) return e;
     // W's rows are read in whole 32-wide k steps
-    if (b.N % GK == 0) return run_mfma<kKRow, kRowK, true>(a, s);
-    return run_fma<kKRow, kRowK, true>(a, true, s);
+    if (b.N % GK == 0) return run_mfma<kKRow, kRowK>(a, s);
+    return run_fma<kKRow, kRowK>(a, true, s);
   }
-  e = run_fma<kKRow, kRowK, false>(w, false, s);
+  e = run_fma<kKRow, kRowK>(w, false, s);
   if (e != hipSuccess) return e;
-  return run_fma<kKRow, kRowK, true>(a, false, s);
+  return run_fma<kKRow, kRowK>(a, false, s);
 }
 
 }  // namespace qkv

@@ -54,7 +54,7 @@ struct BackwardArgs {
   void* dbias;             // nullptr when the plan has no bias
   void* gy;                // scratch [N, Tp] plan dtype: unrotated upstream gradient, transposed
   void* act;               // scratch [T, H] plan dtype: normalised activations
-  float* ga;               // scratch [T, H] fp32: gradient of the activations
+  void* ga;                // scratch [T, H] plan dtype: gradient of the activations
   float* inv_rms;          // scratch [T]
   float* partial;          // scratch [kBackwardPartials, H] fp32 column partial sums
   const double* rev_freq;  // [d/2]
@@ -77,7 +77,7 @@ struct GemmArgs {
   int lda, ldb, ldc;
 };
 // The backward's two GEMMs on this library's kernels: dw [H, N] (plan dtype) = act^T gy
-// and b.ga [T, H] (fp32) = gy W^T; bf16 plans on the matrix cores (ga there when N is a
+// and b.ga [T, H] (plan dtype) = gy W^T; bf16 plans on the matrix cores (ga there when N is a
 // multiple of 32), fp32 plans and other shapes on fp32 FMA tiles.
 hipError_t launch_backward_gemms(const BackwardArgs& b, void* dw, hipStream_t stream);
 int backward_colsum_chunks(int T);

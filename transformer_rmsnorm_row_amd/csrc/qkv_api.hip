@@ -42,7 +42,7 @@ struct Plan {
   // backward scratch, allocated by the first qkv_backward through the plan
   void* bwd_gy;         // [max_tokens, N] plan dtype
   void* bwd_act;        // [max_tokens, H] plan dtype
-  float* bwd_ga;        // [max_tokens, H] fp32
+  void* bwd_ga;         // [max_tokens, H] plan dtype
   float* bwd_partial;   // [kBackwardPartials, H] fp32
   rocblas_handle blas;  // the unfused forward's GEMM (created on its first call)
 };
@@ -142,7 +142,7 @@ qkv_status ensure_backward_scratch(Plan* pl) {
   const size_t tp = (size_t)qkv::backward_token_pitch((int)T);
   bool ok = (pl->bwd_gy || hipMalloc(&pl->bwd_gy, tp * N * elem) == hipSuccess) &&
             (pl->bwd_act || hipMalloc(&pl->bwd_act, T * H * elem) == hipSuccess) &&
-            (pl->bwd_ga || hipMalloc(&pl->bwd_ga, T * H * sizeof(float)) == hipSuccess) &&
+            (pl->bwd_ga || hipMalloc(&pl->bwd_ga, T * H * elem) == hipSuccess) &&
             hipMalloc(&pl->bwd_partial, (size_t)qkv::kBackwardPartials * H * sizeof(float)) == hipSuccess;
   if (!ok) {
     (void)hipGetLastError();
@@ -665,9 +665,7 @@ qkv_status qkv_backward(qkv_plan plan, int64_t num_tokens, const void* x, const 
   for (const void* p : {x, w_norm, w_qkv, dq, dk, dv, (const void*)dx, (const void*)dw_norm, (const void*)dw_qkv})
     if (!aligned(p, 16)) return QKV_ERR_INVALID_ARG;
   if (!aligned(pos, 4) || (dbias && !aligned(dbias, 16))) return QKV_ERR_INVALID_ARG;
-  // the fp32 activation gradient [T, H] is addressed with 32-bit byte offsets too
-  if (num_tokens * pl->desc.hidden * 4 >= kMaxBytes) return QKV_ERR_UNSUPPORTED;
-  // and so is the transposed gradient [N, T rounded up to 32]
+  // the transposed gradient [N, T rounded up to 32] is addressed with 32-bit byte offsets
   if ((int64_t)qkv::backward_token_pitch((int)num_tokens) * pl->N * (pl->bf16 ? 2 : 4) >= kMaxBytes)
     return QKV_ERR_UNSUPPORTED;
   qkv_status st = check_device(pl);
