@@ -18,7 +18,7 @@
 #include <algorithm>
 
 #include "device_common.h"
-#include "launch.h"
+#include "backward.h"
 
 namespace qkv {
 

@@ -43,7 +43,7 @@
 #include <type_traits>
 
 #include "device_common.h"
-#include "launch.h"
+#include "backward.h"
 
 namespace qkv {
 

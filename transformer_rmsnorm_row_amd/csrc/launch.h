@@ -40,52 +40,6 @@ struct ForwardArgs {
   bool prenormed;
 };
 
-// Backward of the chain (see backward.hip): everything but the two GEMMs.
-struct BackwardArgs {
-  const void* x;
-  const void* w_norm;
-  const void* w;           // W_qkv [H, N]
-  const int32_t* pos;
-  const void* dq;
-  const void* dk;
-  const void* dv;
-  void* dx;
-  void* dw_norm;
-  void* dbias;             // nullptr when the plan has no bias
-  void* gy;                // scratch [N, Tp] plan dtype: unrotated upstream gradient, transposed
-  void* act;               // scratch [T, H] plan dtype: normalised activations
-  void* ga;                // scratch [T, H] plan dtype: gradient of the activations
-  float* inv_rms;          // scratch [T]
-  float* partial;          // scratch [kBackwardPartials, H] fp32 column partial sums
-  const double* rev_freq;  // [d/2]
-  int T, H, N, Nq, Nkv, d;
-  float eps;
-  bool bf16;
-};
-constexpr int kBackwardChunks = 64;     // token chunks of the generic column sums
-constexpr int kBackwardPartials = 2048; // partial rows of the fused norm-gradient pass (>= kBackwardChunks)
-// Token pitch of the transposed gradient gy^T [N][Tp]: T rounded up to 32 (pad zero).
-inline int backward_token_pitch(int T) { return (T + 31) / 32 * 32; }
-// One plain GEMM C[M, N] = sum_k A(m, k) B(k, n), fp32 accumulation (gemm.hip).  Each
-// operand is [rows][K] (k contiguous) or [K][cols] per the GEMM's template; pitches in
-// elements.
-struct GemmArgs {
-  const void* a;
-  const void* b;
-  void* c;
-  int M, N, K;
-  int lda, ldb, ldc;
-};
-// The backward's two GEMMs on this library's kernels: dw [H, N] (plan dtype) = act^T gy
-// and b.ga [T, H] (plan dtype) = gy W^T; bf16 plans on the matrix cores (ga there when N is a
-// multiple of 32), fp32 plans and other shapes on fp32 FMA tiles.
-hipError_t launch_backward_gemms(const BackwardArgs& b, void* dw, hipStream_t stream);
-int backward_colsum_chunks(int T);
-// unrotate (gy), activations (a, r) and the bias gradient
-hipError_t launch_backward_pre_gemm(const BackwardArgs& b, hipStream_t stream);
-// dx and the norm-weight gradient, once ga = gy W^T is in b.ga
-hipError_t launch_backward_post_gemm(const BackwardArgs& b, hipStream_t stream);
-
 // One pass over bf16 x [T, H]: xw = bf16(x * w_norm), tiled per 256-row panel and 32-wide
 // k step in the prefill kernel's LDS order (T rounded up to 256 rows, the extra rows zero),
 // and inv_rms[t] = 1/rms of row t.

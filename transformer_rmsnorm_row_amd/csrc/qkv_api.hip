@@ -13,6 +13,7 @@
 
 #include "qkv.h"
 #include "launch.h"
+#include "backward.h"
 #include "unfused.h"
 
 // Device scratch of qkv_forward_noalloc (layout and size next to that entry point).
