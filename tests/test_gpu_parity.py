@@ -127,6 +127,29 @@ def test_prefill_split_k(cid, T, over):
     print(P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], f"{wl.name} split T={T}"))
 
 
+PLAIN_SHAPE_CASES = [
+    # (workload, T, overrides): plain (not split-K) prefill forwards on every head size of
+    # the 128 x 512 single-launch kernel, and on the 256 x 256 normalise-on-load kernel,
+    # which takes projections whose width is a multiple of 256 but not of 512; ragged T
+    (3, 6000, {"hidden": 2048, "num_q_heads": 16, "num_kv_heads": 4, "head_dim": 64}),   # N = 1536
+    (3, 3000, {"hidden": 2048, "num_q_heads": 8, "num_kv_heads": 2, "head_dim": 256}),   # N = 3072
+    (5, 11000, {"hidden": 1024, "num_q_heads": 4, "num_kv_heads": 1}),                   # N = 768, bias
+]
+
+
+@pytest.mark.parametrize("cid,T,over", PLAIN_SHAPE_CASES)
+def test_prefill_plain_head_sizes_and_widths(cid, T, over):
+    """Every element of Q, K and V against the oracle for plain prefill forwards of
+    head size 64 and 256 (128 x 512 kernel) and of a 768-wide projection (256 x 256
+    kernel, normalising on load in one launch)."""
+    wl = shaped(workloads.WORKLOADS[cid].with_tokens(1, T), **over)
+    inp = workloads.make_inputs(wl, seed=13 * T + cid)
+    with qkv.Plan.for_workload(wl) as plan:
+        assert plan.variant(T) == "prefill"
+        got = run(plan, inp)
+    print(P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], f"{wl.name} plain T={T}"))
+
+
 # ---------------------------------------------------------------- ragged sizes, full comparison
 
 MEDIUM = [
