@@ -25,6 +25,8 @@ QKV bias (2 x 8192 tokens).  Besides it the line carries:
   decode        the 64-token decode step streaming its weight from HBM (8 weight
                 copies rotated so the 256 MB last-level cache cannot hold them);
   other_workloads  two mid-size batches (512 tokens on the GQA shape, 128 decode tokens);
+  tp8_shard     one GPU's share of the Llama-7B and GQA prefill forwards under 8-way head
+                sharding (whole heads per GPU, no exchange on this path);
   unfused       the chain as three steps (RMSNorm kernel, rocBLAS GEMM, bias+RoPE
                 kernel) against the fused forward, on the prefill and decode shapes;
   kv_cache, swiglu, backward  the built next steps (K/V into a cache, the gated MLP,
@@ -492,6 +494,32 @@ def other_workloads_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
     return res
 
 
+def shard_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
+    """One GPU's share under 8-way head sharding (tensor parallel, column-parallel W_qkv):
+    each GPU takes whole Q heads and whole K/V heads, x is replicated, and there is no
+    exchange on this path, so one GPU's time at the shard shape is the sharded forward's
+    time.  Llama-7B: 4 Q + 4 K/V heads per GPU (N = 1536); Llama-3-8B GQA: 4 Q + 1 K/V
+    head (N = 768); full T.  Compared with an eighth of the unsharded forward's time."""
+    import dataclasses
+    import torch
+    res = {}
+    for base_name, nq, nkv in (("llama7b_prefill", 4, 4), ("llama3_8b_gqa_prefill", 4, 1)):
+        base = workloads.BY_NAME[base_name]
+        wl = dataclasses.replace(base, name=base_name + "_tp8_shard", num_q_heads=nq, num_kv_heads=nkv)
+        inp = workloads.make_inputs(wl)
+        bufs = device_inputs(wl, inp)
+        with qkv.Plan.for_workload(wl) as plan:
+            variant = plan.variant(wl.tokens)
+            _, sec = time_forward(plan, bufs, steps, warmup)
+        flops = wl.flops()
+        res[wl.name] = {"tokens": wl.tokens, "n": wl.n_total, "variant": variant, "us": round(sec * 1e6, 2),
+                        "tflops": round(flops / sec / 1e12, 2),
+                        "mfma_frac": round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del bufs
+        torch.cuda.empty_cache()
+    return res
+
+
 def prepass_leg(qkv, wl, bufs, steps: int = 30, warmup: int = 5):
     """The same forward through a plan with the opt-in pre-pass form
     (QKV_PLAN_PREFILL_PREPASS): a pre-pass writes bf16(x * w_norm) to HBM and the MFMA
@@ -680,6 +708,8 @@ def main() -> int:
         out["unfused"] = unfused_leg(qkv, workloads)
         print("[bench] other workloads leg", file=sys.stderr, flush=True)
         out["other_workloads"] = other_workloads_leg(qkv, workloads)
+        print("[bench] 8-way head-sharding shard leg", file=sys.stderr, flush=True)
+        out["tp8_shard"] = shard_leg(qkv, workloads)
     del bufs
     torch.cuda.empty_cache()
     if not args.no_extra:
