@@ -9,15 +9,17 @@
 //
 // MFMA form (bf16 operands, fp32 accumulation):
 //   * 256 x 256 output tile per 512-thread workgroup (8 waves, two per SIMD); wave
-//     (g, s) owns rows 128g..+127 and columns 64s..+63: 4 x 2 accumulators of
-//     v_mfma_f32_32x32x16_bf16 (128 fp32 per lane).
+//     (g, s) owns rows 128g..+127 and columns 64s..+63: 8 x 4 accumulators of
+//     v_mfma_f32_16x16x32_bf16 (128 fp32 per lane).  With no conversion in the loop the
+//     16-cycle 16 x 16 x 32 shape, which moves half the accumulator bytes per flop of
+//     the 32 x 32 x 16 one, is the faster of the two at the chip's power limit.
 //   * Each operand is one of two layouts in memory:
 //       kRowK  [rows][K], k contiguous: a step of 32 k is 64 bytes of each of the tile's
 //              256 rows, staged as [256][64 B] with the 16-byte chunks XOR-ed by bits
 //              2..3 of the row, read as fragments with ds_read_b128;
 //       kKRow  [K][cols], cols contiguous: a step is 32 rows of 512 bytes, staged as
-//              loaded with chunk c of k row r at c ^ 4 (r mod 4), read as fragments with
-//              the transpose read ds_read_b64_tr_b16.
+//              loaded with chunk c of k row r at c ^ 2 ((r mod 4) + 4 ((r / 8) mod 4)),
+//              read as fragments with the transpose read ds_read_b64_tr_b16.
 //     Both GEMMs take A as kKRow and B as kRowK, the pairing measured fastest (one
 //     operand of each kind: 623-633 us on 8192 x 4096 x 12288, against 650 us with both
 //     kKRow and 838 us with both kRowK): dW takes a [T, H] and gy^T [N, Tp], ga takes
@@ -28,7 +30,7 @@
 //     operand, wave and step.
 //   * Ping-pong: waves 0-3 and 4-7 are one phase apart.  A memory phase reads the
 //     wave's fragments of step t, issues step t + 3 and waits until its own part of
-//     step t + 1 has landed; a compute phase runs the step's 16 MFMAs.  Barriers
+//     step t + 1 has landed; a compute phase runs the step's 32 MFMAs.  Barriers
 //     separate the phases, so on every SIMD one wave feeds the matrix pipe while the
 //     other reads LDS.
 //   * Tails: loads outside an operand's buffer read zeros (K past the end for kKRow,
@@ -74,8 +76,12 @@ __device__ __forceinline__ void gwait_vmcnt() {
 __device__ __forceinline__ uint32_t rowk_off(uint32_t row, uint32_t chunk) {
   return row * 64u + ((chunk ^ ((row >> 2) & 3u)) << 4);
 }
-// [32][512 B] staging of a kKRow step: chunk c of k row r at c ^ 4 (r mod 4)
-__device__ __forceinline__ uint32_t krow_chunk(uint32_t k, uint32_t c) { return c ^ ((k & 3u) << 2); }
+// [32][512 B] staging of a kKRow step: chunk c of k row r at c ^ 2 ((r mod 4) + 4 ((r / 8)
+// mod 4)), so the 16 k rows of one transpose read (4 per 16-lane group, groups 8 rows
+// apart) fall on distinct banks
+__device__ __forceinline__ uint32_t krow_chunk(uint32_t k, uint32_t c) {
+  return c ^ (((k & 3u) | (((k >> 3) & 3u) << 2)) << 1);
+}
 
 // One operand of the MFMA GEMM: its DMA offsets and fragment reads.  `org` is the
 // tile's first row (kRowK) or column (kKRow) of this operand, `ld` its row pitch in
@@ -132,21 +138,21 @@ struct Operand {
   }
 };
 
-// Fragment of a 32-wide block (rows or columns blk..blk+31 of the operand's 256) for
-// k sub-step ks (k 16 ks .. +15 of the step): lane l gets index blk + l % 32, k 8 (l / 32)
-// .. +7, the operand layout of v_mfma_f32_32x32x16_bf16 for A rows and B columns alike.
+// Fragment of a 16-wide block (rows or columns blk..blk+15 of the operand's 256) for
+// the step's 32 k: lane l gets index blk + l % 16, k 8 (l / 16) .. +7, the operand layout
+// of v_mfma_f32_16x16x32_bf16 for A rows and B columns alike.
 template <int kLayout>
-__device__ __forceinline__ bf16x8 read_frag(const uint8_t* stage_base, uint32_t blk, int ks, int lane) {
+__device__ __forceinline__ bf16x8 read_frag(const uint8_t* stage_base, uint32_t blk, int lane) {
   if constexpr (kLayout == kRowK) {
-    const uint32_t row = blk + ((uint32_t)lane & 31u), chunk = 2u * ks + ((uint32_t)lane >> 5);
+    const uint32_t row = blk + ((uint32_t)lane & 15u), chunk = (uint32_t)lane >> 4;
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage_base + rowk_off(row, chunk)));
   } else {
-    // transpose reads: 16-lane group g covers k rows 8 (g / 2) + 0..3 (+4 for the second
-    // read) and indices 16 (g % 2) + 0..15 of the block; lane j of the group points at
-    // k row j / 4, indices 4 (j % 4) .. +3
+    // transpose reads: 16-lane group g covers k rows 8 g + 0..3 (+4 for the second read)
+    // and the block's 16 indices; lane j of the group points at k row j / 4, indices
+    // 4 (j % 4) .. +3, and receives index j's four k values
     const uint32_t tg = (uint32_t)lane >> 4, tj = (uint32_t)lane & 15u;
-    const uint32_t k = 16u * ks + 8u * (tg >> 1) + (tj >> 2);
-    const uint32_t col = blk + 16u * (tg & 1u) + 4u * (tj & 3u);
+    const uint32_t k = 8u * tg + (tj >> 2);
+    const uint32_t col = blk + 4u * (tj & 3u);
     const uint8_t* p = stage_base + k * 512u + krow_chunk(k, col >> 3) * 16u + (col & 7u) * 2u;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 512));
@@ -184,25 +190,20 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int
   opb.init(g.b, n0, g.ldb, kLB == kRowK ? g.N : g.K, g.K, wave, lane);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
-  f32x16 acc[4][2];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 fa[4][2], fb[2][2];
+  bf16x8 fa[8], fb[4];
   auto read_frags = [&](int stage) {
     const uint8_t* sa = smem + kGABase + stage * kGStep;
     const uint8_t* sb = smem + kGBBase + stage * kGStep;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int rb = 0; rb < 8; ++rb) fa[rb] = read_frag<kLA>(sa, 128u * grp + 16u * rb, lane);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) fa[rb][ks] = read_frag<kLA>(sa, 128u * grp + 32u * rb, ks, lane);
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) fb[cb][ks] = read_frag<kLB>(sb, 64u * slot + 32u * cb, ks, lane);
-    }
+    for (int cb = 0; cb < 4; ++cb) fb[cb] = read_frag<kLB>(sb, 64u * slot + 16u * cb, lane);
   };
   auto issue = [&](int t, int stage) {
     opa.issue(t, stage, lds0 + kGABase, wave);
@@ -245,9 +246,9 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int
     }
     raw_barrier();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int ks = i >> 3, rb = (i >> 1) & 3, cb = i & 1;
-      acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[rb][ks], fb[cb][ks], acc[rb][cb], 0, 0, 0);
+    for (int i = 0; i < 32; ++i) {
+      const int rb = i >> 2, cb = i & 3;
+      acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[rb], fb[cb], acc[rb][cb], 0, 0, 0);
     }
     barrier();
   };
@@ -274,32 +275,32 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue through LDS: the rings are free (every wave's last fragment reads
-  // returned before the last barrier).  Accumulator register r of lane l is row
-  // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of its 32 x 32 block.  Each wave stages
-  // its 128 x 64 results, rounded once to bf16, in a private 16 KB region (128-byte
-  // rows), column bit 5 flipped on rows with bit 2 set (lanes 32-63 write the row 4
-  // below lanes 0-31 and so land on the other banks), reads them back as 16-byte row
-  // pieces and stores those: whole 128-byte lines.
+  // returned before the last barrier).  Accumulator register i of lane l is row
+  // 4 (l / 16) + i, column l % 16 of its 16 x 16 block.  Each wave stages its 128 x 64
+  // results, rounded once to bf16, in a private 16 KB region (128-byte rows), column bits
+  // 4-5 XOR-ed with bits 2-3 of the row (the four 16-lane groups write rows 4 apart,
+  // which then land on different banks), reads them back as 16-byte row pieces and
+  // stores those: whole 128-byte lines.
   uint8_t* ws = smem + wave * 16384;
-  const uint32_t swz = (((uint32_t)lane >> 5) & 1u) << 5;  // (row >> 2) & 1 of every row this lane writes
+  const uint32_t swz = ((uint32_t)lane >> 4) << 4;  // 16 ((row >> 2) & 3) of every row this lane writes
   const auto c_rsrc = make_rsrc(g.c, (uint32_t)g.M * (uint32_t)g.ldc * 2u);
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t row = 32u * rb + 8u * (r >> 2) + 4u * ((uint32_t)lane >> 5) + (r & 3);
-        const uint32_t col = (32u * cb + ((uint32_t)lane & 31u)) ^ swz;
-        // the element is copied out as a float first: a bit cast taken straight from the
-        // vector element stored element 0 of the accumulator for every r
-        const float v = acc[rb][cb][r];
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t row = 16u * rb + 4u * ((uint32_t)lane >> 4) + i;
+        const uint32_t col = (16u * cb + ((uint32_t)lane & 15u)) ^ swz;
+        // the element is copied out as a float first (a bit cast taken straight from a
+        // vector element has been miscompiled)
+        const float v = acc[rb][cb][i];
         *reinterpret_cast<uint16_t*>(ws + row * 128u + col * 2u) = f32_to_bf16(v);
       }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const uint32_t row = 8u * j + ((uint32_t)lane >> 3), q = (uint32_t)lane & 7u;
-    const uint32_t pc = (8u * q) ^ (((row >> 2) & 1u) << 5);
+    const uint32_t pc = (8u * q) ^ (((row >> 2) & 3u) << 4);
     const u32x4 v = *reinterpret_cast<const u32x4*>(ws + row * 128u + pc * 2u);
     const int grow = m0 + 128 * grp + (int)row, gcol = n0 + 64 * slot + 8 * (int)q;
     // rows past M fall outside the buffer's range; columns past N are sent outside it
