@@ -62,6 +62,7 @@ COUNTER_FILE = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = {
     "prefill_wide_kernel": ("prefill_wide.hip", "device_common.h", "launch.h"),
     "prefill_kernel": ("prefill.hip", "rownorm.hip", "device_common.h", "launch.h"),
+    "prefill_pre_kernel": ("gemm.hip", "prefill_pre.h", "backward.h", "rownorm.hip", "device_common.h", "launch.h"),
     "decode_kernel": ("decode.hip", "device_common.h", "launch.h"),
 }
 
@@ -332,6 +333,11 @@ def unfused_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
         xn, y = bufs
         fused = _event_time(lambda: plan.forward(x, w, W, b, pos, out=(q, k, v)), steps, warmup)
         unfused = _event_time(lambda: plan.forward_unfused(x, w, W, b, pos, out=bufs), steps, warmup)
+        pair = None
+        if wl.tokens > 256:
+            with qkv.Plan.for_workload(wl, prefill_prepass=True) as pp:
+                if pp.variant(wl.tokens) == "prefill":
+                    pair = _event_time(lambda: pp.forward(x, w, W, b, pos, out=(q, k, v)), steps, warmup)
         norm = _event_time(lambda: plan.rms_norm(x, w, out=xn), steps, warmup)
         rope = _event_time(lambda: plan.rope(y, b, pos), steps, warmup)
         wn = torch.ones(wl.head_dim, dtype=wl.torch_dtype, device=x.device)
@@ -342,13 +348,16 @@ def unfused_leg(qkv, workloads, steps: int = 30, warmup: int = 5):
         unfused_bytes = fused_bytes + 2 * T * H * e + 2 * T * N * e
         res[name] = {"tokens": T, "fused_us": round(fused * 1e6, 2), "unfused_us": round(unfused * 1e6, 2),
                      "unfused_over_fused": round(unfused / fused, 3),
+                     "prepass_pair_us": None if pair is None else round(pair * 1e6, 2),
+                     "unfused_over_prepass_pair": None if pair is None else round(unfused / pair, 3),
                      "rms_norm_us": round(norm * 1e6, 2), "rope_us": round(rope * 1e6, 2),
                      "head_norm_rope_us": round(norm_rope * 1e6, 2),
                      "gemm_us_by_difference": round((unfused - norm - rope) * 1e6, 2),
                      "rms_norm_hbm_GBps": round(2 * T * H * e / norm / 1e9, 1),
                      "rope_hbm_GBps": round(2 * T * N * e / rope / 1e9, 1),
                      "algorithmic_bytes_fused": fused_bytes, "algorithmic_bytes_unfused": unfused_bytes,
-                     "kernels": "fused: 1 launch; unfused: norm kernel, rocBLAS GEMM, rotation kernel"}
+                     "kernels": "fused: 1 launch; opt-in pre-pass pair: pre-pass + 256 x 256 MFMA kernel; "
+                                "unfused: norm kernel, rocBLAS GEMM, rotation kernel"}
         del x, w, W, b, pos, q, k, v, xn, y, bufs, wn
         torch.cuda.empty_cache()
     return res
@@ -638,7 +647,7 @@ def main() -> int:
         bound, achieved, unit = "mfma", flops / kernel_s / 1e12, "TFLOP/s"
     traffic = measured_traffic(wl.name + ("+prepass" if prepass_form else ""))
     # the launches of one forward, all inside the HIP-event window that gives kernel_us
-    kernels = {"prefill": ("prenorm_kernel + prefill_kernel (opt-in pre-pass form)" if prepass_form else
+    kernels = {"prefill": ("prenorm_kernel + prefill_pre_kernel (opt-in pre-pass form)" if prepass_form else
                            "prefill_wide_kernel (one launch, normalise-on-load)"),
                "prefill_split": "prefill_kernel (split-K form)",
                "decode": "decode_kernel", "generic": "generic kernel"}.get(variant, variant)

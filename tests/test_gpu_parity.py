@@ -150,6 +150,54 @@ def test_prefill_plain_head_sizes_and_widths(cid, T, over):
     print(P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], f"{wl.name} plain T={T}"))
 
 
+PREPASS_CASES = [
+    # (workload, T, overrides): the opt-in pre-pass form's 256 x 256 kernel on every head
+    # size, ragged T, with bias; T large enough that the plain (not split-K) form runs
+    (3, 1500, {"hidden": 1024}),                                                        # GQA, N = 6144
+    (3, 6000, {"hidden": 2048, "num_q_heads": 16, "num_kv_heads": 4, "head_dim": 64}),  # N = 1536
+    (3, 3000, {"hidden": 512, "num_q_heads": 8, "num_kv_heads": 2, "head_dim": 256}),   # N = 3072
+    (5, 777, {"hidden": 1024}),                                                         # MHA + bias
+]
+
+
+@pytest.mark.parametrize("cid,T,over", PREPASS_CASES)
+def test_prefill_prepass_shapes(cid, T, over):
+    """Every element of Q, K and V against the oracle for the opt-in pre-pass form
+    (pre-pass, then the pre-normalised 256 x 256 kernel) at every head size."""
+    wl = shaped(workloads.WORKLOADS[cid].with_tokens(1, T), **over)
+    inp = workloads.make_inputs(wl, seed=17 * T + cid)
+    with qkv.Plan.for_workload(wl, prefill_prepass=True) as plan:
+        assert plan.variant(T) == "prefill"
+        got = run(plan, inp)
+    print(P.assert_parity(got, P.oracle_forward(wl, inp), P.TOL["bf16"], f"{wl.name} pre-pass T={T}"))
+
+
+def test_prefill_prepass_kv_cache():
+    """The pre-pass form writing K and V into cache slots: the cache rows equal the dense
+    forward's K and V bit for bit, unnamed rows stay untouched, Q is unchanged."""
+    wl = shaped(workloads.WORKLOADS[3].with_tokens(1, 1500), hidden=1024)
+    inp = workloads.make_inputs(wl, seed=4242)
+    rows = 2048
+    g = torch.Generator().manual_seed(5)
+    slots = torch.randperm(rows, generator=g)[:wl.tokens].to(torch.int32)
+    slots[::97] = -1          # some tokens write no K/V
+    with qkv.Plan.for_workload(wl, prefill_prepass=True) as plan:
+        assert plan.variant(wl.tokens) == "prefill"
+        q, k, v = run(plan, inp)
+        kc = torch.full((rows, wl.n_kv), 7.0, dtype=torch.bfloat16, device=DEV)
+        vc = torch.full_like(kc, 7.0)
+        args = [inp[n].to(DEV) for n in ("x", "w_norm", "w_qkv")]
+        qc = plan.forward_kv_cache(*args, None, inp["pos"].to(DEV), slots.to(DEV), kc, vc)
+        torch.cuda.synchronize()
+    assert torch.equal(qc, q)
+    keep = slots >= 0
+    idx = slots[keep].long().to(DEV)
+    assert torch.equal(kc[idx], k[keep.to(DEV)]) and torch.equal(vc[idx], v[keep.to(DEV)])
+    untouched = torch.ones(rows, dtype=torch.bool)
+    untouched[slots[keep].long()] = False
+    assert bool((kc[untouched.to(DEV)] == 7.0).all()) and bool((vc[untouched.to(DEV)] == 7.0).all())
+
+
 # ---------------------------------------------------------------- ragged sizes, full comparison
 
 MEDIUM = [

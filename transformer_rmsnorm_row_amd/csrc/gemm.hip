@@ -16,7 +16,7 @@
 //   * Each operand is one of two layouts in memory:
 //       kRowK  [rows][K], k contiguous: a step of 32 k is 64 bytes of each of the tile's
 //              256 rows, staged as [256][64 B] with the 16-byte chunks XOR-ed by bits
-//              2..3 of the row, read as fragments with ds_read_b128;
+//              1..2 of the row, read as fragments with ds_read_b128;
 //       kKRow  [K][cols], cols contiguous: a step is 32 rows of 512 bytes, staged as
 //              loaded with chunk c of k row r at c ^ 2 ((r mod 4) + 4 ((r / 8) mod 4)),
 //              read as fragments with the transpose read ds_read_b64_tr_b16.
@@ -46,6 +46,7 @@
 
 #include "device_common.h"
 #include "backward.h"
+#include "prefill_pre.h"
 
 namespace qkv {
 
@@ -63,7 +64,10 @@ constexpr int kGLds = 2 * kGStages * kGStep;  // 128 KB
 constexpr int kGGroupM = 8;
 constexpr uint32_t kOutside = 0x80000000u;  // a byte offset past every operand (all are < 2^31 bytes)
 
-constexpr int kRowK = 0, kKRow = 1;
+// kTiled: the pre-pass's bf16(x * w_norm), stored per 256-row panel and 32-wide k step
+// in exactly the kRowK staging order ([panels][K / 32][256 rows][64 B], chunk c of row r
+// at c ^ ((r >> 1) & 3)), so each DMA instruction reads 1 KB of consecutive bytes.
+constexpr int kRowK = 0, kKRow = 1, kTiled = 2;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -74,9 +78,12 @@ __device__ __forceinline__ void gwait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-// [256][64 B] staging of a kRowK step: chunk c of row r at c ^ ((r >> 2) & 3)
+// [256][64 B] staging of a kRowK step: chunk c of row r at c ^ ((r >> 1) & 3).  Bits 1-2
+// of the row leave the 16 x 16 x 32 fragment reads (lane l: row l % 16, chunk l / 16)
+// free of bank conflicts; bits 2-3 cost about 4 conflict cycles per read (measured:
+// 19.9% of the pre-normalised kernel's CU cycles).
 __device__ __forceinline__ uint32_t rowk_off(uint32_t row, uint32_t chunk) {
-  return row * 64u + ((chunk ^ ((row >> 2) & 3u)) << 4);
+  return row * 64u + ((chunk ^ ((row >> 1) & 3u)) << 4);
 }
 // [32][512 B] staging of a kKRow step: chunk c of k row r at c ^ 2 ((r mod 4) + 4 ((r / 8)
 // mod 4)), so the 16 k rows of one transpose read (4 per 16-lane group, groups 8 rows
@@ -106,8 +113,12 @@ struct Operand {
         // instruction i of wave w fills rows 32w + 16i .. +15; lane l physical chunk l % 4
         // of row 32w + 16i + l / 4
         const uint32_t r = 32u * wave + 16u * i + (lane >> 2);
-        const uint32_t c = ((uint32_t)lane & 3u) ^ ((r >> 2) & 3u);
+        const uint32_t c = ((uint32_t)lane & 3u) ^ ((r >> 1) & 3u);
         voff[i] = ((uint32_t)org + r) * ld2 + c * 16u;
+      } else if constexpr (kLayout == kTiled) {
+        // the panel of rows org .. org + 255 (org a multiple of 256), then the same 1 KB
+        // as in LDS: instruction i of wave w, 16 bytes per lane
+        voff[i] = (uint32_t)(org / 256) * (uint32_t)K * 512u + (32u * wave + 16u * i) * 64u + 16u * (uint32_t)lane;
       } else {
         // instruction i of wave w fills k rows 4w + 2i, +1; lane l physical chunk l % 32
         // of row 4w + 2i + l / 32
@@ -129,6 +140,9 @@ struct Operand {
       if constexpr (kLayout == kRowK) {
         dst = lds_base + (uint32_t)stage * kGStep + (32u * wave + 16u * i) * 64u;
         off = k0 * 2u < kbytes ? voff[i] + k0 * 2u : kOutside;
+      } else if constexpr (kLayout == kTiled) {
+        dst = lds_base + (uint32_t)stage * kGStep + (32u * wave + 16u * i) * 64u;
+        off = voff[i] + (uint32_t)t * (uint32_t)kGStep;
       } else {
         dst = lds_base + (uint32_t)stage * kGStep + (4u * wave + 2u * i) * 512u;
         off = voff[i] + k0 * ld2;
@@ -145,7 +159,7 @@ struct Operand {
 // of v_mfma_f32_16x16x32_bf16 for A rows and B columns alike.
 template <int kLayout>
 __device__ __forceinline__ bf16x8 read_frag(const uint8_t* stage_base, uint32_t blk, int lane) {
-  if constexpr (kLayout == kRowK) {
+  if constexpr (kLayout == kRowK || kLayout == kTiled) {
     const uint32_t row = blk + ((uint32_t)lane & 15u), chunk = (uint32_t)lane >> 4;
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stage_base + rowk_off(row, chunk)));
   } else {
@@ -165,11 +179,10 @@ __device__ __forceinline__ bf16x8 read_frag(const uint8_t* stage_base, uint32_t 
 template <int N>
 using GInt = std::integral_constant<int, N>;
 
-template <int kLA, int kLB>
-__global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int nk) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kGLds];
-
-  // ---- tile: XCD-contiguous numbering, then groups of kGGroupM row panels
+// Tile (m0, n0) of workgroup blockIdx.x: XCD-contiguous numbering, then groups of
+// kGGroupM row panels, so the ~32 workgroups resident on one XCD share operand steps
+// in its L2.
+__device__ __forceinline__ void gemm_tile(int tiles_m, int tiles_n, int& m0, int& n0) {
   const int G = tiles_m * tiles_n;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, local = bid >> 3;
@@ -179,20 +192,20 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int
   const int first_m = group * kGGroupM;
   const int gm = min(tiles_m - first_m, kGGroupM);
   const int idx = L - group * kGGroupM * tiles_n;
-  const int m0 = (first_m + idx % gm) * GM, n0 = (idx / gm) * GN;
+  m0 = (first_m + idx % gm) * GM;
+  n0 = (idx / gm) * GN;
+}
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2, slot = wave & 3;
-
-  Operand<kLA> opa;
-  Operand<kLB> opb;
-  // A: rows m of the result; kRowK holds them as rows of length K, kKRow as columns
-  opa.init(g.a, m0, g.lda, kLA == kRowK ? g.M : g.K, g.K, wave, lane);
-  opb.init(g.b, n0, g.ldb, kLB == kRowK ? g.N : g.K, g.K, wave, lane);
+// The K loop of one 256 x 256 tile: wave (g = wave / 4) accumulates rows 128 g .. +127 of
+// the tile against the four 16-column blocks of B that start at tile columns bcol[0..3],
+// as 8 x 4 accumulators of v_mfma_f32_16x16x32_bf16.  `hook` runs once, after the last
+// load has landed (t = nk - 2), to request the epilogue's inputs under the last two steps.
+// On return every load has landed and every fragment read has returned.
+template <int kLA, int kLB, class Hook>
+__device__ __forceinline__ void mfma_loop(Operand<kLA>& opa, Operand<kLB>& opb, uint8_t* smem, int nk, int wave,
+                                          int lane, const uint32_t (&bcol)[4], f32x4 (&acc)[8][4], Hook&& hook) {
+  const int grp = wave >> 2;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-
-  f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -205,7 +218,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb) fa[rb] = read_frag<kLA>(sa, 128u * grp + 16u * rb, lane);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) fb[cb] = read_frag<kLB>(sb, 64u * slot + 16u * cb, lane);
+    for (int cb = 0; cb < 4; ++cb) fb[cb] = read_frag<kLB>(sb, bcol[cb], lane);
   };
   auto issue = [&](int t, int stage) {
     opa.issue(t, stage, lds0 + kGABase, wave);
@@ -245,6 +258,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int
       gwait_vmcnt<kOps>();
     } else if constexpr (kMode == 2) {
       gwait_vmcnt<0>();
+      hook();
     }
     raw_barrier();
 #pragma unroll
@@ -275,6 +289,26 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int
   step(GInt<3>{}, t + 3, GInt<3>{});
   if (grp == 0) barrier();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int kLA, int kLB>
+__global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int nk) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kGLds];
+  int m0, n0;
+  gemm_tile(tiles_m, tiles_n, m0, n0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, slot = wave & 3;
+
+  Operand<kLA> opa;
+  Operand<kLB> opb;
+  // A: rows m of the result; kRowK holds them as rows of length K, kKRow as columns
+  opa.init(g.a, m0, g.lda, kLA == kRowK ? g.M : g.K, g.K, wave, lane);
+  opb.init(g.b, n0, g.ldb, kLB == kRowK ? g.N : g.K, g.K, wave, lane);
+  // wave (g, s) owns columns 64 s .. +63
+  const uint32_t bcol[4] = {64u * slot, 64u * slot + 16u, 64u * slot + 32u, 64u * slot + 48u};
+  f32x4 acc[8][4];
+  mfma_loop(opa, opb, smem, nk, wave, lane, bcol, acc, [] {});
 
   // ---- epilogue through LDS: the rings are free (every wave's last fragment reads
   // returned before the last barrier).  Accumulator register i of lane l is row
@@ -308,6 +342,159 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int
     // rows past M fall outside the buffer's range; columns past N are sent outside it
     const uint32_t off = gcol < g.N ? ((uint32_t)grow * (uint32_t)g.ldc + (uint32_t)gcol) * 2u : kOutside;
     buf_store16(v, c_rsrc, off);
+  }
+}
+
+// ---- the pre-normalised QKV forward on the same loop (the opt-in pre-pass form): A is
+// the pre-pass's tiled bf16(x * w_norm) [T_pad, H], B the weight [H, N].  Wave (g, s)
+// holds rows 128 g .. +127 and two 32-column halves d/2 apart, so both members of every
+// rotation pair sit in the same lane and register of accumulator blocks cb and cb + 2.
+// Epilogue: y = acc * r[t] + bias, Q and K pairs rotated with cos/sin of
+// pos * theta^(-2i/d) (turn count in fp64, hardware sin/cos on the fraction of a turn),
+// rounded once to bf16, staged per wave through LDS and stored as 16-byte row pieces;
+// K and V rows optionally to key/value-cache slots.
+template <int kD>
+__device__ __forceinline__ int pre_first_half(int s) {
+  static_assert(kD == 64 || kD == 128 || kD == 256, "head sizes of the kernel");
+  return kD == 128 ? 128 * (s >> 1) + 32 * (s & 1) : (kD == 256 ? 32 * s : 64 * s);
+}
+
+template <int kD>
+__global__ __launch_bounds__(kGThreads, 1) void prefill_pre_kernel(ForwardArgs a, int tiles_m, int tiles_n, int nk) {
+  // the rings, then (epilogue) 8 per-wave staging regions over them and the row information
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kGLds + 3 * GM * 4];
+  static_assert(8 * 16384 <= kGLds, "staging regions inside the rings");
+  int m0, n0;
+  gemm_tile(tiles_m, tiles_n, m0, n0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, slot = wave & 3;
+  const int H = a.H, N = a.N, T = a.T;
+  const int T_pad = tiles_m * GM;
+
+  Operand<kTiled> opa;
+  Operand<kKRow> opb;
+  opa.init(a.x, m0, H, T_pad, H, wave, lane);
+  opb.init(a.w, n0, N, H, H, wave, lane);
+  const int fb = pre_first_half<kD>(slot);
+  const uint32_t bcol[4] = {(uint32_t)fb, (uint32_t)fb + 16u, (uint32_t)(fb + kD / 2), (uint32_t)(fb + kD / 2 + 16)};
+
+  // The epilogue's inputs, requested once the last load has landed: 1/rms, position and
+  // cache slot of row tid (tid < 256), the bias of the lane's four columns and the
+  // rotation frequencies of its two pairs.  Range-checked loads need no branch (rows
+  // past T read 0, a plan without bias reads 0 through an empty range).
+  float rinv_pref = 0.f;
+  int32_t pos_pref = 0, slot_pref = -1;
+  uint16_t braw[4] = {0, 0, 0, 0};
+  uint64_t rev_bits[2] = {0, 0};
+  auto prefetch = [&]() {
+    const int row = (int)((uint32_t)(m0 + (tid & (GM - 1))) * 4u);
+    rinv_pref = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.inv_rms, (uint32_t)T * 4u), row, 0, 0));
+    pos_pref = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.pos, (uint32_t)T * 4u), row, 0, 0);
+    slot_pref = __builtin_amdgcn_raw_buffer_load_b32(
+        make_rsrc(a.slots ? a.slots : a.pos, a.slots ? (uint32_t)T * 4u : 0u), row, 0, 0);
+    const auto b_rsrc = make_rsrc(a.bias ? a.bias : a.w, a.bias ? (uint32_t)N * 2u : 0u);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+      braw[cb] = __builtin_amdgcn_raw_buffer_load_b16(b_rsrc, (int)((uint32_t)(n0 + (int)bcol[cb] + (lane & 15)) * 2u), 0, 0);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+      rev_bits[cb] = __builtin_bit_cast(
+          uint64_t, __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(a.rev_freq, (kD / 2) * 8u),
+                                                         (int)((uint32_t)(fb % kD + 16 * cb + (lane & 15)) * 8u), 0, 0));
+  };
+  f32x4 acc[8][4];
+  mfma_loop(opa, opb, smem, nk, wave, lane, bcol, acc, prefetch);
+
+  // ---- epilogue (the rings are free: every fragment read returned before the loop's
+  // last barrier).  Row information of the tile's 256 rows after the 8 staging regions.
+  __syncthreads();
+  float* s_rinv = reinterpret_cast<float*>(smem + 8 * 16384);
+  int32_t* s_pos = reinterpret_cast<int32_t*>(smem + 8 * 16384 + GM * 4);
+  int32_t* s_slot = reinterpret_cast<int32_t*>(smem + 8 * 16384 + GM * 8);
+  if (tid < GM) {
+    s_rinv[tid] = rinv_pref;
+    s_pos[tid] = pos_pref;
+    s_slot[tid] = m0 + tid < T ? slot_pref : -1;  // rows past T write nothing
+  }
+  __syncthreads();
+  float bv[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) bv[cb] = bf16_to_f32(braw[cb]);
+  const double rev[2] = {__builtin_bit_cast(double, rev_bits[0]), __builtin_bit_cast(double, rev_bits[1])};
+  // the wave's head lies in one of Q, K, V (their column counts are multiples of the head
+  // size): Q and K heads are rotated, V heads not
+  const int hcol = n0 + fb;
+  const bool rotate = hcol < a.Nq + a.Nkv;
+  // Staging: the wave's 128 x 64 results (columns 0-31 the first half, 32-63 the second)
+  // in a private 16 KB region of 128-byte rows, column bits 4-5 XOR-ed with bits 2-3 of
+  // the row (the four 16-lane groups write rows 4 apart, which then land on different
+  // banks).  Accumulator register i of lane l is row 4 (l / 16) + i, column l % 16 of its
+  // 16 x 16 block.
+  uint8_t* ws = smem + wave * 16384;
+  const uint32_t swz = ((uint32_t)lane >> 4) << 4;
+  auto scale_rotate_stage = [&](auto RotC) {
+    constexpr bool kRot = decltype(RotC)::value;
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lrow = 16u * rb + 4u * ((uint32_t)lane >> 4) + i;
+          const int trow = 128 * grp + (int)lrow;
+          const float ri = s_rinv[trow];
+          float y0 = fmaf(acc[rb][cb][i], ri, bv[cb]);
+          float y1 = fmaf(acc[rb][cb + 2][i], ri, bv[cb + 2]);
+          if constexpr (kRot) {
+            double t = (double)s_pos[trow] * rev[cb];
+            const float tf = (float)(t - floor(t));
+            const float c = __builtin_amdgcn_cosf(tf), s = __builtin_amdgcn_sinf(tf);
+            const float u0 = y0, v0 = y1;
+            y0 = u0 * c - v0 * s;
+            y1 = v0 * c + u0 * s;
+          }
+          const uint32_t c0 = (16u * cb + ((uint32_t)lane & 15u)) ^ swz, c1 = (32u + 16u * cb + ((uint32_t)lane & 15u)) ^ swz;
+          *reinterpret_cast<uint16_t*>(ws + lrow * 128u + c0 * 2u) = f32_to_bf16(y0);
+          *reinterpret_cast<uint16_t*>(ws + lrow * 128u + c1 * 2u) = f32_to_bf16(y1);
+        }
+      }
+    }
+  };
+  if (rotate)
+    scale_rotate_stage(std::true_type{});
+  else
+    scale_rotate_stage(std::false_type{});
+
+  void* out;
+  uint32_t width, ocol;
+  if (hcol < a.Nq) {
+    out = a.q; width = a.Nq; ocol = hcol;
+  } else if (hcol < a.Nq + a.Nkv) {
+    out = a.k; width = a.Nkv; ocol = hcol - a.Nq;
+  } else {
+    out = a.v; width = a.Nkv; ocol = hcol - a.Nq - a.Nkv;
+  }
+  const bool to_cache = a.slots != nullptr && hcol >= a.Nq;
+  const uint32_t out_rows = to_cache ? (uint32_t)a.cache_rows : (uint32_t)T;
+  const auto ro = make_rsrc(out, out_rows * width * 2u);
+  // 16-byte pieces: 8 per 128-byte staged row, pieces 0-3 to the first half's columns
+  // and 4-7 to the second half's (d/2 further)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t lrow = 8u * j + ((uint32_t)lane >> 3), q = (uint32_t)lane & 7u;
+    const uint32_t pc = (8u * q) ^ (((lrow >> 2) & 3u) << 4);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ws + lrow * 128u + pc * 2u);
+    const int trow = 128 * grp + (int)lrow;
+    uint32_t orow = (uint32_t)(m0 + trow);
+    if (to_cache) {
+      const int32_t sr = s_slot[trow];
+      orow = sr >= 0 && sr < a.cache_rows ? (uint32_t)sr : out_rows;
+    } else if (m0 + trow >= T) {
+      orow = out_rows;  // past the buffer's range: dropped
+    }
+    const uint32_t col = ocol + (q < 4 ? 8u * q : (uint32_t)(kD / 2) + 8u * (q - 4));
+    buf_store16(v, ro, (orow * width + col) * 2u);
   }
 }
 
@@ -393,6 +580,23 @@ hipError_t run_fma(const GemmArgs& g, bool bf16, hipStream_t s) {
 }
 
 }  // namespace
+
+bool prefill_pre_supports(int H, int N, int d) {
+  return (d == 64 || d == 128 || d == 256) && N % GN == 0 && H % 128 == 0 && H >= 128;
+}
+
+hipError_t launch_prefill_pre(const ForwardArgs& a, hipStream_t s) {
+  if (!a.prenormed || !prefill_pre_supports(a.H, a.N, a.d)) return hipErrorInvalidValue;
+  const int tiles_m = (a.T + GM - 1) / GM, tiles_n = a.N / GN, nk = a.H / GK;
+  const dim3 grid(tiles_m * tiles_n), block(kGThreads);
+  if (a.d == 64)
+    prefill_pre_kernel<64><<<grid, block, 0, s>>>(a, tiles_m, tiles_n, nk);
+  else if (a.d == 256)
+    prefill_pre_kernel<256><<<grid, block, 0, s>>>(a, tiles_m, tiles_n, nk);
+  else
+    prefill_pre_kernel<128><<<grid, block, 0, s>>>(a, tiles_m, tiles_n, nk);
+  return hipGetLastError();
+}
 
 hipError_t launch_backward_gemms(const BackwardArgs& b, void* dw, hipStream_t s) {
   const int tp = backward_token_pitch(b.T);

@@ -35,14 +35,14 @@ struct ForwardArgs {
   float eps;
   bool bf16;
   // x holds bf16(x * w_norm) pre-tiled and inv_rms each row's 1/rms, written by
-  // launch_prenorm: the plain prefill kernel then loads activations like the weight, with
-  // no conversion
+  // launch_prenorm: the opt-in pre-pass form's MFMA kernel (launch_prefill_pre) then loads
+  // the activations like the weight, with no conversion
   bool prenormed;
 };
 
 // One pass over bf16 x [T, H]: xw = bf16(x * w_norm), tiled per 256-row panel and 32-wide
-// k step in the prefill kernel's LDS order (T rounded up to 256 rows, the extra rows zero),
-// and inv_rms[t] = 1/rms of row t.
+// k step in the LDS order of the pre-pass form's MFMA kernel (T rounded up to 256 rows, the
+// extra rows zero), and inv_rms[t] = 1/rms of row t.
 hipError_t launch_prenorm(const void* x, const void* w_norm, void* xw, float* inv_rms, int T, int H, float eps,
                           hipStream_t stream);
 hipError_t launch_inv_rms(const void* x, float* inv_rms, int T, int H, float eps, bool bf16,

@@ -1,17 +1,16 @@
 // bf16 MFMA prefill kernel for gfx950 on 256 x 256 tiles: RMS row reduction,
 // normalise-on-load QKV projection, bias and rotate-half rotary embedding, Q/K/V
 // written once.  It serves the prefill shapes the 128 x 512 kernel of prefill_wide.hip
-// does not take, the split-K form for token counts too small to fill the chip, the gated
-// MLP epilogue, and the opt-in pre-normalised form (activations normalised once into a
-// plan buffer by a pre-pass, then loaded like the weight).
+// does not take, the split-K form for token counts too small to fill the chip, and the
+// gated MLP epilogue.
 //
 // The method is the fused RMSNorm + QKV projection + RoPE kernel of the page
 // "Liger-Kernel底层优化：新一代内核级推理加速引擎介绍" (section
 // "融合内核是如何工作的？来看一段简化版实现", and the fused-kernel list that names
 // "Fused RMSNorm + QKV Projection + RoPE"): the sum of squares over the hidden size
 // gives each token's 1/rms, the bias is added to each dot product, and each rotation pair
-// (i, i + head_dim/2) is turned by the position's angle before the single store.  In the
-// default form the normalised activations exist only inside the kernel.
+// (i, i + head_dim/2) is turned by the position's angle before the single store.  The
+// normalised activations exist only inside the kernel.
 //
 // gfx950 design (the listing's one-thread-per-feature loop is not used):
 //   * 256 x 256 output tile per 512-thread workgroup (8 waves, two per SIMD).  Wave
@@ -33,21 +32,11 @@
 //     a 2-deep activation ring; the same registers give the row sums of squares, so
 //     1/rms needs no separate pass.  1/rms scales the accumulator rows in the
 //     epilogue, which is the same product (diag(r) X diag(w) W = diag(r) (X diag(w)) W).
-//   * Pre-normalised form (kPre), the one plain prefill forwards use: a one-pass
-//     pre-kernel writes bf16(x * w_norm) and each row's 1/rms (the same products and
-//     rounding), laid out per 256-row panel and 32-wide step exactly as the LDS holds a
-//     step, and this kernel then streams the activation steps global -> LDS by DMA like
-//     the weight (4-deep ring, 3 steps ahead, 1 KB of consecutive bytes per
-//     instruction), with no register staging and no conversion in the loop; 1/rms
-//     comes from the pre-pass.  The pre-pass costs
-//     one read and one write of x, and saves more than that: 48 column tiles no longer
-//     each redo the conversion of the same rows.
 //   * All vector-memory instructions of the loop are inline assembly with waits
 //     counted at compile time, so prefetches stay in flight across barriers.
 //   * Tiles are numbered so that the ~32 workgroups running at once on one XCD
 //     (workgroups go round-robin over the 8 XCDs) cover 4 row panels x 8 column
-//     panels (2 x 16 for the pre-normalised form on wide projections) and share them
-//     in that XCD's L2.
+//     panels and share them in that XCD's L2.
 //   * Epilogue: y = acc * r[t] + bias; Q and K pairs rotated with cos/sin of
 //     pos * theta^(-2i/d) (turn count reduced in fp64, hardware sin/cos on the
 //     fraction of a turn); bf16 results staged through LDS and stored with 16-byte
@@ -74,7 +63,6 @@ constexpr int kThreads = 512;
 constexpr int kStep = BM * BK * 2;                  // bytes of one [256][32] or [32][256] bf16 step
 constexpr int kWStages = 4;                         // weight steps: DMA issued 3 steps ahead
 constexpr int kAStages = 2;                         // converted activation steps
-constexpr int kAStagesPre = 4;                      // pre-normalised activation steps: DMA 3 ahead
 constexpr int kWBase = 0;
 constexpr int kABase = kWStages * kStep;
 constexpr int kStagePitch = 272;                    // 128 bf16 + 16 B pad per staged output row
@@ -82,13 +70,10 @@ constexpr int kBlockStage = 128 * kStagePitch;      // one group's 128 rows x on
 constexpr int kRowInfo = 4 * kBlockStage;           // per-row pos, 1/rms, cache slot after the staging area
 constexpr int kLds = kRowInfo + BM * 12;
 static_assert(kABase + kAStages * kStep <= kLds, "loop rings must fit");
-static_assert(kABase + kAStagesPre * kStep <= kLds, "loop rings must fit");
 static_assert(kLds <= 160 * 1024, "LDS budget of one workgroup");
-// Row panels per tile group: 4, or 2 for the pre-normalised form with at least 48
-// column tiles (measured on the 12288-column shapes: 686 -> 666 us and 1358 -> 1293 us;
-// 2 was slower for the 6144-column GQA shape and for the normalise-on-load gated MLP).
+// Row panels per tile group (2 was slower for the 6144-column GQA shape and for the
+// gated MLP).
 constexpr int kGroupM = 4;
-constexpr int kGroupMWide = 2;
 
 // LDS byte offset of 16-byte chunk `chunk` (0..3) of row `row` in a [256][32] bf16
 // activation step (64 B rows).  The chunk index is XOR-ed with bits 2..3 of the row,
@@ -151,9 +136,8 @@ __device__ __forceinline__ int pair_block(int slot) {
 // 256 rows' partial sums of squares.
 constexpr int kPartFloats = BM * BN + BM;
 
-template <int kEpi, int kD, int kSplit, bool kPre = false>
+template <int kEpi, int kD, int kSplit>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int tiles_m, int tiles_n) {
-  static_assert(!kPre || (kEpi == kEpiQkv && kSplit == 1), "pre-normalised form: plain QKV kernel only");
   constexpr bool kSplitK = kSplit > 1;
   constexpr int nsplit = kSplit;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
@@ -172,7 +156,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     const int q8 = G >> 3, r8 = G & 7;
     L = (xcd < r8) ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
   }
-  const int group_m = (kPre && tiles_n >= 48) ? kGroupMWide : kGroupM;
+  const int group_m = kGroupM;
   const int group = L / (group_m * tiles_n);
   const int first_m = group * group_m;
   const int gm = min(tiles_m - first_m, group_m);
@@ -220,21 +204,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     }
     b_voff[i] = ((kofs + 4u * wave + krow) * N + col) * 2u;
   }
-  // ---- pre-normalised activation DMA (kPre): the pre-pass stored each 256-row panel's
-  // 32-wide k steps as [256 rows][64 B] images already in a_off's swizzled order, so wave
-  // w's instruction i copies the 1 KB of rows 32w + 16i .. +15 of a step as it lies.
-  uint32_t xa_voff[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    xa_voff[i] = (uint32_t)tm * (uint32_t)H * 512u + (32u * wave + 16u * i) * 64u + (uint32_t)lane * 16u;
   const uint64_t wbase = reinterpret_cast<uint64_t>(a.w);
   const u32x4 w_rsrc = {(uint32_t)wbase, (uint32_t)(wbase >> 32), (uint32_t)H * (uint32_t)N * 2u,
                         (uint32_t)kBufferWord3};
   const uint64_t xbase = reinterpret_cast<uint64_t>(a.x), nbase = reinterpret_cast<uint64_t>(a.w_norm);
   const u32x4 x_rsrc = {(uint32_t)xbase, (uint32_t)(xbase >> 32), (uint32_t)T * (uint32_t)H * 2u, (uint32_t)kBufferWord3};
-  // the pre-tiled activations span whole 256-row panels
-  const u32x4 xa_rsrc = {(uint32_t)xbase, (uint32_t)(xbase >> 32), (uint32_t)tiles_m * (uint32_t)H * 512u,
-                         (uint32_t)kBufferWord3};
   const u32x4 n_rsrc = {(uint32_t)nbase, (uint32_t)(nbase >> 32), (uint32_t)H * 2u, (uint32_t)kBufferWord3};
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
@@ -289,17 +263,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     gx[set][1] = asm_load16(x_voff + x_jstep + k0 * 2u, x_rsrc);
     gw[set] = asm_load16((kofs + k0 + kc * 8u) * 2u, n_rsrc);
   };
-  auto issue_a = [&](int t, int astage) {
-    const uint32_t k0 = (uint32_t)t * BK;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + kABase + astage * kStep + (32 * wave + 16 * i) * 64);
-      const uint32_t voff = xa_voff[i] + k0 * 512u;  // step t's image starts t * 16 KB into the panel
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(voff), "s"(xa_rsrc)
-                   : "m0");
-    }
-  };
-  constexpr int kWOps = 2, kXOps = 3, kAOps = 2;
+  constexpr int kWOps = 2, kXOps = 3;
   // the registers of a set become usable only after an explicit wait
   auto tie_set = [&](int set) { asm volatile("" : "+v"(gx[set][0]), "+v"(gx[set][1]), "+v"(gw[set])); };
 
@@ -401,26 +365,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     constexpr int P = decltype(Pc)::value;
     constexpr int kMode = decltype(ModeC)::value;
     constexpr bool kLast = kMode == 3;
-    if constexpr (kPre) {
-      // both operands by DMA, 3 steps ahead into 4-deep rings; per wave the order is
-      // ..., A(t + 1), W(t + 1), A(t + 2), W(t + 2), A(t + 3), W(t + 3), so this wave's
-      // parts of step t + 1 are complete once at most the 8 of t + 2 and t + 3 are
-      // outstanding.  No conversion: the compute phase is the MFMAs alone.
-      read_frags(P, P);
-      if constexpr (kMode == 0) {
-        issue_a(t + 3, (P + 3) & 3);
-        issue_w(t + 3, (P + 3) & 3);
-        wait_vmcnt<2 * (kAOps + kWOps)>();
-      } else if constexpr (kMode == 1) {
-        wait_vmcnt<kAOps + kWOps>();
-      } else if constexpr (kMode == 2) {
-        wait_vmcnt<0>();
-      }
-      raw_barrier();
-      compute(0, 0, false);
-      barrier();
-      return;
-    }
     read_frags(P & 1, P);
     // memory phase: only this wave's part of W(t + 1) has to be complete at its end
     if constexpr (kMode == 0) {
@@ -454,11 +398,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   int32_t pos_pref = 0, slot_pref = -1;
   uint16_t braw[2] = {0, 0};
   uint64_t rev_bits = 0;
-  float rinv_pref = 0.f;
-  if constexpr (kPre)
-    rinv_pref = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                              make_rsrc(a.inv_rms, (uint32_t)T * 4u),
-                                              (int)((uint32_t)(m0 + (tid & (BM - 1))) * 4u), 0, 0));
   if constexpr (kEpi == kEpiQkv) {
     pos_pref = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.pos, (uint32_t)T * 4u),
                                                     (int)((uint32_t)(m0 + (tid & (BM - 1))) * 4u), 0, 0);
@@ -471,16 +410,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
     rev_bits = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(a.rev_freq, (kD / 2) * 8u),
                                                                                  (int)((uint32_t)(c0 + fl) * 8u), 0, 0));
   }
-  if constexpr (kPre) {
-    // prologue: A(0..2) and W(0..2) issued; this wave's parts of step 0 landed
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      issue_a(s, s);
-      issue_w(s, s);
-    }
-    wait_vmcnt<2 * (kAOps + kWOps)>();
-    barrier();
-  } else {
   // prologue: W(0..2) and x(0..1) issued, x(0) converted into activation slot 0
   issue_w(0, 0);
   issue_x(0, 0);
@@ -506,7 +435,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   barrier();
-  }
   // waves 4-7 start one phase late: their memory phase runs under the compute
   // phase of waves 0-3 and the other way round
   if (grp == 1) barrier();
@@ -527,30 +455,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
   // Every load has landed by now (step K/32 - 2 waited for all of them); the wait, tied
   // to the staging registers, keeps the compiler from handing those registers to the
   // epilogue ahead of it.
-  if constexpr (kPre)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)"
-                 : "+v"(gx[0][0]), "+v"(gx[0][1]), "+v"(gw[0]), "+v"(gx[1][0]), "+v"(gx[1][1]), "+v"(gw[1])
-                 :
-                 : "memory");
+  asm volatile("s_waitcnt vmcnt(0)"
+               : "+v"(gx[0][0]), "+v"(gx[0][1]), "+v"(gw[0]), "+v"(gx[1][0]), "+v"(gx[1][1]), "+v"(gw[1])
+               :
+               : "memory");
   __syncthreads();
   int32_t* s_pos = reinterpret_cast<int32_t*>(smem + kRowInfo);
   float* s_rinv = reinterpret_cast<float*>(smem + kRowInfo + BM * 4);
   int32_t* s_slot = reinterpret_cast<int32_t*>(smem + kRowInfo + BM * 8);
   {
-    if constexpr (kPre) {
-      if (tid < BM) s_rinv[tid] = rinv_pref;  // from the pre-pass
-    } else {
-      // the four lanes holding the chunks of a row are adjacent (kc = lane % 4)
+    // the four lanes holding the chunks of a row are adjacent (kc = lane % 4)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float v = ss[j];
-        v += __shfl_xor(v, 1, 64);
-        v += __shfl_xor(v, 2, 64);
-        // the split-K form keeps the raw partial sum until the slices are added
-        if (kc == 0) s_rinv[arow + 64u * j] = kSplitK ? v : rsqrtf(v / (float)H + a.eps);
-      }
+    for (int j = 0; j < 2; ++j) {
+      float v = ss[j];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      // the split-K form keeps the raw partial sum until the slices are added
+      if (kc == 0) s_rinv[arow + 64u * j] = kSplitK ? v : rsqrtf(v / (float)H + a.eps);
     }
     if (tid < BM) {
       s_pos[tid] = pos_pref;
@@ -772,14 +693,13 @@ hipError_t launch_prefill_d(const ForwardArgs& a, int tiles_m, int tiles_n, hipS
   const int tiles = tiles_m * tiles_n, s = prefill_splits(a, tiles);
   if (s == 2)
     prefill_kernel<kEpiQkv, kD, 2><<<dim3(tiles * 2), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
-  else if (a.prenormed)
-    prefill_kernel<kEpiQkv, kD, 1, true><<<dim3(tiles), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
   else
     prefill_kernel<kEpiQkv, kD, 1><<<dim3(tiles), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(const ForwardArgs& a, hipStream_t stream) {
+  if (a.prenormed) return hipErrorInvalidValue;  // the pre-pass form runs launch_prefill_pre
   const int tiles_m = (a.T + BM - 1) / BM, tiles_n = a.N / BN;
   if (a.d == 64) return launch_prefill_d<64>(a, tiles_m, tiles_n, stream);
   if (a.d == 256) return launch_prefill_d<256>(a, tiles_m, tiles_n, stream);

@@ -14,6 +14,7 @@
 #include "qkv.h"
 #include "launch.h"
 #include "backward.h"
+#include "prefill_pre.h"
 #include "unfused.h"
 
 // Device scratch of qkv_forward_noalloc (layout and size next to that entry point).
@@ -223,7 +224,7 @@ qkv_status launch_forward(Plan* pl, int64_t num_tokens, const void* x, const voi
         if (e != hipSuccess) break;
         a.x = pl->xw;
         a.prenormed = true;
-        e = qkv::launch_prefill(a, s);
+        e = qkv::launch_prefill_pre(a, s);  // takes every shape of the plain prefill variant
       } else if (qkv::prefill_wide_supports(a.H, a.N, a.Nq, a.Nkv, a.d)) {
         e = qkv::launch_prefill_wide(a, s);  // one launch, normalise-on-load
       } else {

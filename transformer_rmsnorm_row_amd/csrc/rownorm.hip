@@ -44,11 +44,11 @@ __global__ __launch_bounds__(256) void inv_rms_kernel(const void* __restrict__ x
   if (lane == 0) out[row] = rsqrtf(ss / (float)H + eps);
 }
 
-// Pre-pass of the prefill kernel's pre-normalised form: the same row reduction, and
+// Pre-pass of the opt-in pre-normalised form: the same row reduction, and
 // the normalise-on-load product bf16(x * w_norm) written out pre-tiled in the order the
 // kernel's LDS holds it, so that each of its activation DMA instructions reads 1 KB of
 // consecutive bytes.  Tiled layout: [T_pad / 256 panels][H / 32 steps][256 rows][4 x 16 B],
-// 16-byte chunk q (k = 8q .. 8q + 7 of the step) of row r stored at chunk q ^ ((r / 4) % 4).
+// 16-byte chunk q (k = 8q .. 8q + 7 of the step) of row r stored at chunk q ^ ((r / 2) % 4).
 // One wavefront per row (rows T .. T_pad - 1 of the last panel are written as zeros),
 // 16-byte loads and stores.
 __global__ __launch_bounds__(256) void prenorm_kernel(const void* __restrict__ x, const void* __restrict__ w,
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void prenorm_kernel(const void* __restrict__ x
   if (row >= T_pad) return;
   const uint32_t row_bytes = (uint32_t)H * 2u;  // multiple of 16 (H % 8 == 0)
   const char* base = (const char*)x + (size_t)row * row_bytes;
-  const uint32_t r = (uint32_t)row & 255u, swz = (r >> 2) & 3u;
+  const uint32_t r = (uint32_t)row & 255u, swz = (r >> 1) & 3u;
   char* panel = (char*)xw + (size_t)(row >> 8) * 256u * row_bytes;
   float ss0 = 0.f, ss1 = 0.f;
 #pragma unroll 4
