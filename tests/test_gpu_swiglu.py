@@ -64,7 +64,9 @@ def _run(wl, inp):
 
 
 @pytest.mark.parametrize("T,H,inter", [(300, 128, 128), (777, 384, 256), (513, 1152, 640), (1, 256, 128),
-                                       (256, 512, 384)])
+                                       (256, 512, 384),
+                                       # 2I a multiple of 512: the 128 x 512 single-launch kernel
+                                       (1000, 512, 768), (129, 256, 256), (2049, 1024, 1280)])
 def test_swiglu_parity(T, H, inter):
     wl, inp = _inputs(T, H, inter, seed=T + H + inter)
     got = _run(wl, inp)

@@ -74,6 +74,10 @@ hipError_t launch_decode(const ForwardArgs& a, hipStream_t stream);
 // N = 2I, T, H, eps, bf16
 hipError_t launch_swiglu(const ForwardArgs& a, hipStream_t stream);
 bool swiglu_supports(int H, int I);
+// the same on the 128 x 512 kernel of prefill_wide.hip, which launch_swiglu picks when 2I is
+// a multiple of 512 (and H of 128)
+hipError_t launch_swiglu_wide(const ForwardArgs& a, hipStream_t stream);
+bool swiglu_wide_supports(int H, int I);
 bool decode_supports(int T, int H, int N, int Nq, int Nkv, int d);
 // fp32 elements of plan scratch the decode kernel needs (partials + sums of squares)
 size_t decode_scratch_floats(int H, int N);

@@ -723,6 +723,7 @@ bool swiglu_supports(int H, int I) { return H % (4 * BK) == 0 && I % 128 == 0; }
 
 hipError_t launch_swiglu(const ForwardArgs& a, hipStream_t stream) {
   // a.N = 2I columns of [gate | up]; the output (a.q) is [T, I]
+  if (swiglu_wide_supports(a.H, a.N / 2)) return launch_swiglu_wide(a, stream);  // one 128 x 512 launch
   const int tiles_m = (a.T + BM - 1) / BM, tiles_n = a.N / BN;
   prefill_kernel<kEpiSwiglu, 128, 1><<<dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
   return hipGetLastError();

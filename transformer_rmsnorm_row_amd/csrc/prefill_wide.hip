@@ -125,8 +125,13 @@ __device__ __forceinline__ int first_half(int w) {
   return kD == 128 ? 128 * (w >> 1) + 32 * (w & 1) : (kD == 256 ? 256 * (w >> 2) + 32 * (w & 3) : 64 * w);
 }
 
-template <int kD>
+// kGlu: the gated MLP on the same loop (post-attention RMSNorm, then [gate | up] and
+// SiLU(gate) * up).  A tile covers 256 features: each 128-column "head" h holds gate
+// features 64 h .. +63 and the same up features 64 columns to the right, so a wave's two
+// halves (d/2 = 64 apart) are the gate and up sums of the same features.
+template <int kD, bool kGlu = false>
 __global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(ForwardArgs a, int tiles_m, int tiles_n) {
+  static_assert(!kGlu || kD == 128, "gated MLP: 64-feature halves");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
 
   // ---- tile selection: XCD-contiguous numbering, then groups of kGroupM row panels
@@ -165,7 +170,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(ForwardArgs a
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t kr = 4u * wave + i;
-    b_voff[i] = (kr * N + n0 + 8u * (lane ^ w_swz(kr))) * 2u;
+    uint32_t col = n0 + 8u * (lane ^ w_swz(kr));
+    if constexpr (kGlu) {
+      // logical chunk c: head c / 16, column 8 (c % 16) of it, gate below 64, up above
+      const uint32_t c = lane ^ w_swz(kr), wi = (c & 15u) * 8u;
+      const uint32_t f = 256u * (uint32_t)tn + 64u * (c >> 4) + (wi & 63u);
+      col = wi < 64u ? f : (uint32_t)(N / 2) + f;
+    }
+    b_voff[i] = (kr * N + col) * 2u;
   }
   const uint64_t wbase = reinterpret_cast<uint64_t>(a.w);
   const u32x4 w_rsrc = {(uint32_t)wbase, (uint32_t)(wbase >> 32), (uint32_t)H * (uint32_t)N * 2u,
@@ -297,6 +309,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(ForwardArgs a
   uint16_t braw[4] = {0, 0, 0, 0};
   uint64_t rev_bits[2] = {0, 0};
   auto prefetch_epilogue = [&]() {
+    if constexpr (kGlu) return;  // the gated MLP needs only 1/rms
     pos_pref = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.pos, (uint32_t)T * 4u),
                                                     (int)((uint32_t)(m0 + (tid & (WM - 1))) * 4u), 0, 0);
     slot_pref = __builtin_amdgcn_raw_buffer_load_b32(
@@ -427,6 +440,43 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(ForwardArgs a
   }
   __syncthreads();
 
+  if constexpr (kGlu) {
+    // ---- gated-MLP epilogue: out = SiLU(g) * u with g, u the gate and up sums scaled by
+    // 1/rms; staged as bf16 in two 128-feature blocks, stored with 16-byte writes to
+    // out [T, N / 2]
+    const int fbase = 64 * (wave >> 1) + 32 * (wave & 1);  // the wave's first feature in the tile
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) {
+      const int rbase = 16 * rb + 4 * (lane >> 4);
+      const f32x4 ri4 = *reinterpret_cast<const f32x4*>(s_rinv + rbase);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int fc = fbase + 16 * cb + (lane & 15);
+        uint8_t* st = smem + (fc >> 7) * kStageBlock + (fc & 127) * 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float g = acc[rb][cb][i] * ri4[i], up = acc[rb][cb + 2][i] * ri4[i];
+          const float o = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * up;
+          *reinterpret_cast<uint16_t*>(st + (rbase + i) * kStagePitch) = f32_to_bf16(o);
+        }
+      }
+    }
+    __syncthreads();
+    // wave w stores rows 32 (w % 4) .. + 31 of feature block w / 4: 16 lanes of 16 bytes
+    // per 256-byte row; rows past T fall outside the buffer's range
+    const uint32_t I = (uint32_t)N / 2u;
+    const auto ro = make_rsrc(a.q, (uint32_t)T * I * 2u);
+    const int blk = wave >> 2;
+    const uint8_t* stage = smem + blk * kStageBlock;
+    const uint32_t ch = lane & 15;
+    const uint32_t fcol = 256u * (uint32_t)tn + 128u * (uint32_t)blk;
+#pragma unroll 4
+    for (int it = 0; it < 8; ++it) {
+      const uint32_t row = 32u * (wave & 3) + 4u * it + (lane >> 4);
+      const u32x4 v = lds_read16(stage, row * kStagePitch + ch * 16u);
+      buf_store16(v, ro, (((uint32_t)m0 + row) * I + fcol + ch * 8u) * 2u);
+    }
+  } else {
   // ---- epilogue: scale, bias, rotate, stage as bf16 per 128-column block, store
   float bcol[4];
 #pragma unroll
@@ -501,6 +551,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(ForwardArgs a
     }
     buf_store16(v, ro, (orow * width + ocol + ch * 8u) * 2u);
   }
+  }
 }
 
 }  // namespace
@@ -508,6 +559,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(ForwardArgs a
 bool prefill_wide_supports(int H, int N, int Nq, int Nkv, int d) {
   return (d == 64 || d == 128 || d == 256) && H % (4 * WK) == 0 && N % WN == 0 && Nq % 128 == 0 &&
          Nkv % 128 == 0 && Nq % d == 0 && Nkv % d == 0;
+}
+
+bool swiglu_wide_supports(int H, int I) { return H % (4 * WK) == 0 && (2 * I) % WN == 0; }
+
+hipError_t launch_swiglu_wide(const ForwardArgs& a, hipStream_t stream) {
+  // a.N = 2I columns of [gate | up]; the output (a.q) is [T, I]
+  if (!swiglu_wide_supports(a.H, a.N / 2)) return hipErrorInvalidValue;
+  const int tiles_m = (a.T + WM - 1) / WM, tiles_n = a.N / WN;
+  prefill_wide_kernel<128, true><<<dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill_wide(const ForwardArgs& a, hipStream_t stream) {
