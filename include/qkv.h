@@ -109,7 +109,8 @@ typedef struct qkv_plan_desc {
  * the current device and return an opaque handle in *out_plan.
  * Returns QKV_ERR_INVALID_ARG for a malformed descriptor or null pointers,
  * QKV_ERR_UNSUPPORTED for shapes outside the kernels (head_dim not a multiple of 8,
- * tensors whose byte size reaches 2^31), QKV_ERR_HIP when no device is usable and
+ * tensors whose byte size reaches 2^31, with QKV_PLAN_PREFILL_PREPASS also a pre-pass
+ * buffer of 2^31 bytes or more), QKV_ERR_HIP when no device is usable and
  * QKV_ERR_OUT_OF_MEMORY when the scratch cannot be allocated.  On error *out_plan is
  * left NULL. */
 qkv_status qkv_plan_create(const qkv_plan_desc* desc, qkv_plan* out_plan);

@@ -180,6 +180,30 @@ def test_token_limit_is_exact(shape):
         assert qkv.load_library().qkv_plan_destroy(h) == qkv.QKV_OK
 
 
+@pytest.mark.parametrize("hidden", [8192, 4096])
+def test_prepass_buffer_limit_is_exact(hidden):
+    """The pre-pass form keeps bf16(x * w_norm) for max_tokens rows rounded up to whole
+    256-row panels; that buffer is addressed with 32-bit byte offsets too, so the first
+    token count whose padded buffer reaches 2^31 bytes is refused before any HIP call
+    even where the tensors themselves stay below the bound, and the last count whose
+    padded buffer fits gets past validation."""
+    shape = dict(hidden=hidden, num_q_heads=8, num_kv_heads=8, head_dim=128, dtype=1)
+    n = 3 * 8 * 128
+    rows = (1 << 31) // (hidden * 2)              # padded rows that reach 2^31 bytes
+    first_bad = rows - 255                         # rounds up to `rows`
+    assert first_bad < (1 << 31) // (max(n, hidden) * 2)  # the tensors alone would pass
+    st, h = _create(max_tokens=first_bad, **shape)
+    assert st in (qkv.QKV_OK, qkv.QKV_ERR_HIP, qkv.QKV_ERR_OUT_OF_MEMORY)
+    if st == qkv.QKV_OK:
+        assert qkv.load_library().qkv_plan_destroy(h) == qkv.QKV_OK
+    st, h = _create(max_tokens=first_bad, flags=qkv.QKV_PLAN_PREFILL_PREPASS, **shape)
+    assert st == qkv.QKV_ERR_UNSUPPORTED and h.value is None
+    st, h = _create(max_tokens=first_bad - 1, flags=qkv.QKV_PLAN_PREFILL_PREPASS, **shape)
+    assert st in (qkv.QKV_OK, qkv.QKV_ERR_HIP, qkv.QKV_ERR_OUT_OF_MEMORY)
+    if st == qkv.QKV_OK:
+        assert qkv.load_library().qkv_plan_destroy(h) == qkv.QKV_OK
+
+
 def _noalloc(desc, T, ptrs=None, bias=None):
     lib = qkv.load_library()
     p = ptrs if ptrs is not None else [16] * 8  # x, w_norm, w_qkv, pos, q, k, v (16-byte aligned dummies)

@@ -80,6 +80,10 @@ qkv_status check_desc(const qkv_plan_desc* d) {
   const int64_t widest = N > d->hidden ? N : d->hidden;
   if (d->max_tokens >= kMaxBytes / (widest * elem)) return QKV_ERR_UNSUPPORTED;
   if ((int64_t)d->hidden * N * elem >= kMaxBytes) return QKV_ERR_UNSUPPORTED;
+  // The pre-pass buffer holds bf16 rows padded to whole 256-row panels.
+  if ((d->flags & QKV_PLAN_PREFILL_PREPASS) != 0 &&
+      (d->max_tokens + 255) / 256 * 256 * (int64_t)d->hidden * 2 >= kMaxBytes)
+    return QKV_ERR_UNSUPPORTED;
   return QKV_OK;
 }
 
