@@ -40,8 +40,8 @@
 //   * All vector-memory instructions of the loop are inline assembly with waits counted
 //     at compile time, so prefetches stay in flight across barriers.
 //   * Tiles are numbered so that the ~32 workgroups running at once on one XCD
-//     (workgroups go round-robin over the 8 XCDs) cover 4 (or 8) row panels x 8 (or 4)
-//     column panels and share their x and W steps in that XCD's L2.
+//     (workgroups go round-robin over the 8 XCDs) cover 6 row panels x 5-6 column panels
+//     (8 x 4 for narrow projections) and share their x and W steps in that XCD's L2.
 //   * Epilogue: y = acc * r[t] + bias; Q and K pairs rotated with cos/sin of
 //     pos * theta^(-2i/d) (turn count reduced in fp64, hardware sin/cos on the fraction
 //     of a turn); bf16 results staged through LDS and stored with 16-byte writes, K and V
@@ -71,11 +71,13 @@ constexpr int kRowInfo = 4 * kStageBlock;    // per-row pos, 1/rms, cache slot a
 constexpr int kEpiLds = kRowInfo + WM * 12;
 constexpr int kLds = kLoopLds > kEpiLds ? kLoopLds : kEpiLds;
 static_assert(kLds <= 160 * 1024, "LDS budget of one workgroup");
-// Row panels per tile group (the tiles of a group are numbered row panel fastest): 4 for
-// projections of 24 or more column tiles, 8 for narrower ones (measured, single launch:
-// Llama-7B 702 -> 695-699 us and Qwen-7B 1392-1398 -> 1356 us with 4; the 12-column-tile
-// GQA shape 363-365 us with 8 against 369 with 4).
-constexpr int kGroupMWide = 4, kGroupMNarrow = 8;
+// Row panels per tile group (the tiles of a group are numbered row panel fastest): 6 for
+// projections of 24 or more column tiles, 8 for narrower ones.  Measured, single launch, us
+// per forward, groups of 2 / 3 / 4 / 6 row panels on one box, then 4 / 5 / 6 / 7 / 8 / 12 /
+// 16 on a slower one: Qwen-7B 1417 / 1394 / 1363 / 1351, then 1403 / 1404 / 1391 / 1389-1398 /
+// 1416 / 1393 / 1395; Llama-7B 731 / 714 / 699 / 692, then 719 / 714 / 713 / 712 / 716 / 710 /
+// 720.  The 12-column-tile GQA shape: 366 us with groups of 8 or 16, 369 with 4 or 6.
+constexpr int kGroupMWide = 6, kGroupMNarrow = 8;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
