@@ -59,9 +59,13 @@ constexpr int kGStages = 4;
 constexpr int kGABase = 0;
 constexpr int kGBBase = kGStages * kGStep;
 constexpr int kGLds = 2 * kGStages * kGStep;  // 128 KB
-// Row panels per tile group, measured on the whole backward of the Llama-7B shape: 2 / 4 / 8 /
-// 16 panels -> 1472-1492 / 1428-1451 / 1421-1436 / 1452-1470 us.
-constexpr int kGGroupM = 8;
+// Row panels per tile group.  The backward's products, measured on the whole backward of the
+// Llama-7B shape: 2 / 4 / 8 / 16 panels -> 1472-1492 / 1428-1451 / 1421-1436 / 1452-1470 us,
+// and on another box 3 / 5 / 6 / 8 / 12 -> 1493-1518 / 1487-1505 / 1466-1487 / 1452-1473 /
+// 1476-1494 us.  The pre-pass form's kernel, same box (Qwen-7B, Llama-7B pairs): 3 / 5 / 6 / 8 /
+// 12 -> 1190 / 1185-1186 / 1189-1191 / 1190-1191 / 1211-1212 us and 617 / 612-613 / 612-615 /
+// 621-623 / 619-623 us.
+constexpr int kGGroupM = 8, kGPreGroupM = 5;
 constexpr uint32_t kOutside = 0x80000000u;  // a byte offset past every operand (all are < 2^31 bytes)
 
 // kTiled: the pre-pass's bf16(x * w_norm), stored per 256-row panel and 32-wide k step
@@ -180,18 +184,19 @@ template <int N>
 using GInt = std::integral_constant<int, N>;
 
 // Tile (m0, n0) of workgroup blockIdx.x: XCD-contiguous numbering, then groups of
-// kGGroupM row panels, so the ~32 workgroups resident on one XCD share operand steps
+// kGroup row panels, so the ~32 workgroups resident on one XCD share operand steps
 // in its L2.
+template <int kGroup>
 __device__ __forceinline__ void gemm_tile(int tiles_m, int tiles_n, int& m0, int& n0) {
   const int G = tiles_m * tiles_n;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, local = bid >> 3;
   const int q8 = G >> 3, r8 = G & 7;
   const int L = (xcd < r8) ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
-  const int group = L / (kGGroupM * tiles_n);
-  const int first_m = group * kGGroupM;
-  const int gm = min(tiles_m - first_m, kGGroupM);
-  const int idx = L - group * kGGroupM * tiles_n;
+  const int group = L / (kGroup * tiles_n);
+  const int first_m = group * kGroup;
+  const int gm = min(tiles_m - first_m, kGroup);
+  const int idx = L - group * kGroup * tiles_n;
   m0 = (first_m + idx % gm) * GM;
   n0 = (idx / gm) * GN;
 }
@@ -295,7 +300,7 @@ template <int kLA, int kLB>
 __global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int nk) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kGLds];
   int m0, n0;
-  gemm_tile(tiles_m, tiles_n, m0, n0);
+  gemm_tile<kGGroupM>(tiles_m, tiles_n, m0, n0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2, slot = wave & 3;
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_pre_kernel(ForwardArgs a
   __shared__ __attribute__((aligned(16))) uint8_t smem[kGLds + 3 * GM * 4];
   static_assert(8 * 16384 <= kGLds, "staging regions inside the rings");
   int m0, n0;
-  gemm_tile(tiles_m, tiles_n, m0, n0);
+  gemm_tile<kGPreGroupM>(tiles_m, tiles_n, m0, n0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2, slot = wave & 3;
