@@ -134,14 +134,19 @@ PLAIN_SHAPE_CASES = [
     (3, 6000, {"hidden": 2048, "num_q_heads": 16, "num_kv_heads": 4, "head_dim": 64}),   # N = 1536
     (3, 3000, {"hidden": 2048, "num_q_heads": 8, "num_kv_heads": 2, "head_dim": 256}),   # N = 3072
     (5, 11000, {"hidden": 1024, "num_q_heads": 4, "num_kv_heads": 1}),                   # N = 768, bias
+    # more tiles than the single-launch kernel's one workgroup per CU: some workgroups
+    # take a second tile (288 tiles) or most do (480)
+    (2, 1500, {}),                                                                        # Llama-7B shape
+    (3, 5000, {}),                                                                        # GQA shape
 ]
 
 
 @pytest.mark.parametrize("cid,T,over", PLAIN_SHAPE_CASES)
 def test_prefill_plain_head_sizes_and_widths(cid, T, over):
     """Every element of Q, K and V against the oracle for plain prefill forwards of
-    head size 64 and 256 (128 x 512 kernel) and of a 768-wide projection (256 x 256
-    kernel, normalising on load in one launch)."""
+    head size 64 and 256 (128 x 512 kernel), of a 768-wide projection (256 x 256
+    kernel, normalising on load in one launch), and of tile counts that are not a
+    multiple of the 128 x 512 kernel's grid."""
     wl = shaped(workloads.WORKLOADS[cid].with_tokens(1, T), **over)
     inp = workloads.make_inputs(wl, seed=13 * T + cid)
     with qkv.Plan.for_workload(wl) as plan:
@@ -510,10 +515,12 @@ def test_variant_names():
                 assert v == "prefill"
 
 
-@pytest.mark.parametrize("cid,T,variant", [(3, 300, "prefill_split"), (3, 2048, "prefill"), (4, 150, "decode")])
+@pytest.mark.parametrize("cid,T,variant", [(3, 300, "prefill_split"), (3, 2048, "prefill"), (3, 3000, "prefill"),
+                                           (4, 150, "decode")])
 def test_graph_replays(cid, T, variant):
-    """A forward captured in a HIP graph (split-K prefill; plain prefill, one launch; decode
-    over a 128-token and a 22-token chunk): each of several replays, with
+    """A forward captured in a HIP graph (split-K prefill; plain prefill, one launch, with
+    fewer and with more tiles than workgroups; decode over a 128-token and a 22-token
+    chunk): each of several replays, with
     eager forwards of other inputs in between, writes exactly the eager result; the kernels
     leave their arrival counters at zero for the next call."""
     wl = workloads.WORKLOADS[cid].with_tokens(1, T) if cid == 3 else workloads.WORKLOADS[cid].with_tokens(T, 1)

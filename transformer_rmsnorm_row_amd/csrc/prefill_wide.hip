@@ -39,6 +39,8 @@
 //     (diag(r) X diag(w) W = diag(r) (X diag(w)) W).
 //   * All vector-memory instructions of the loop are inline assembly with waits counted
 //     at compile time, so prefetches stay in flight across barriers.
+//   * Persistent over tiles: one workgroup per CU walks its tiles in turn, so a tile's
+//     start does not wait for a new workgroup to be dispatched.
 //   * Tiles are numbered so that the ~32 workgroups running at once on one XCD
 //     (workgroups go round-robin over the 8 XCDs) cover 6 row panels x 5-6 column panels
 //     (8 x 4 for narrow projections) and share their x and W steps in that XCD's L2.
@@ -46,6 +48,7 @@
 //     pos * theta^(-2i/d) (turn count reduced in fp64, hardware sin/cos on the fraction
 //     of a turn); bf16 results staged through LDS and stored with 16-byte writes, K and V
 //     rows optionally to key/value-cache slots.
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -131,14 +134,14 @@ __device__ __forceinline__ int first_half(int w) {
 // SiLU(gate) * up).  A tile covers 256 features: each 128-column "head" h holds gate
 // features 64 h .. +63 and the same up features 64 columns to the right, so a wave's two
 // halves (d/2 = 64 apart) are the gate and up sums of the same features.
-template <int kD, bool kGlu = false>
-__global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(ForwardArgs a, int tiles_m, int tiles_n) {
+// One output tile: the tile that workgroup `bid` of a grid of tiles_m * tiles_n would own.
+template <int kD, bool kGlu>
+__device__ __forceinline__ void wide_tile(const ForwardArgs& a, int tiles_m, int tiles_n, int bid) {
   static_assert(!kGlu || kD == 128, "gated MLP: 64-feature halves");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
 
   // ---- tile selection: XCD-contiguous numbering, then groups of kGroupM row panels
   const int G = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
   const int xcd = bid & 7, local = bid >> 3;
   const int q8 = G >> 3, r8 = G & 7;
   const int L = (xcd < r8) ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
@@ -151,7 +154,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(ForwardArgs a
   const int tn = idx / gm;
   const int m0 = tm * WM, n0 = tn * WN;
 
-  const int tid = threadIdx.x;
+  // The thread index is made opaque to the compiler, so that nothing derived from it
+  // is hoisted out of the caller's tile loop and kept live (in spilled registers)
+  // across tiles.
+  int tid_opaque = threadIdx.x;
+  asm volatile("" : "+v"(tid_opaque));
+  const int tid = tid_opaque;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int grp = wave >> 2;
@@ -556,6 +564,41 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(ForwardArgs a
   }
 }
 
+// Persistent over tiles: a grid of at most one workgroup per CU (a multiple of 8, so a
+// workgroup's XCD is the same for all its tiles) walks the tiles in the order a grid of
+// one workgroup per tile would start them, so the workgroups running at once on an XCD
+// still share a tile group.  No workgroup waits for another.  Against one workgroup per
+// tile (measured, outputs bit-identical; two boxes): Qwen-7B 1368-1369 -> 1343-1344 and
+// 1333-1334 -> 1317-1318 us, Llama-7B 698-700 -> 684-686 and 683-684 -> 666-667 us, the
+// GQA shape 371 -> 364 and 362 -> 355.5 us, the Llama-7B gated MLP 1241-1243 -> 1217-1218
+// and 1209-1212 -> 1185-1190 us.
+template <int kD, bool kGlu = false>
+__global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(ForwardArgs a, int tiles_m, int tiles_n) {
+  const int G = tiles_m * tiles_n;
+  for (int vb = blockIdx.x; vb < G; vb += (int)gridDim.x) {
+    wide_tile<kD, kGlu>(a, tiles_m, tiles_n, vb);
+    __syncthreads();  // the next tile's first weight steps overwrite the output staging
+  }
+}
+
+// Workgroups of a launch over G tiles on the current device: one per CU (rounded down to
+// a multiple of 8), or G if that is fewer.  The CU count is looked up once per device (a
+// device attribute query, no stream work, so a forward under graph capture may run it);
+// should the query fail, every tile gets a workgroup of its own, which is also correct.
+int wide_grid(int G) {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return G;
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) return G;
+    c = n - n % 8;
+    cus[dev].store(c, std::memory_order_relaxed);
+  }
+  return G < c ? G : c;
+}
+
 }  // namespace
 
 bool prefill_wide_supports(int H, int N, int Nq, int Nkv, int d) {
@@ -569,13 +612,13 @@ hipError_t launch_swiglu_wide(const ForwardArgs& a, hipStream_t stream) {
   // a.N = 2I columns of [gate | up]; the output (a.q) is [T, I]
   if (!swiglu_wide_supports(a.H, a.N / 2)) return hipErrorInvalidValue;
   const int tiles_m = (a.T + WM - 1) / WM, tiles_n = a.N / WN;
-  prefill_wide_kernel<128, true><<<dim3(tiles_m * tiles_n), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
+  prefill_wide_kernel<128, true><<<dim3(wide_grid(tiles_m * tiles_n)), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_wide(const ForwardArgs& a, hipStream_t stream) {
   const int tiles_m = (a.T + WM - 1) / WM, tiles_n = a.N / WN;
-  const dim3 grid(tiles_m * tiles_n), block(kThreads);
+  const dim3 grid(wide_grid(tiles_m * tiles_n)), block(kThreads);
   if (a.d == 64)
     prefill_wide_kernel<64><<<grid, block, 0, stream>>>(a, tiles_m, tiles_n);
   else if (a.d == 256)
