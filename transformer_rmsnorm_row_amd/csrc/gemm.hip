@@ -183,13 +183,12 @@ __device__ __forceinline__ bf16x8 read_frag(const uint8_t* stage_base, uint32_t 
 template <int N>
 using GInt = std::integral_constant<int, N>;
 
-// Tile (m0, n0) of workgroup blockIdx.x: XCD-contiguous numbering, then groups of
+// Tile (m0, n0) that workgroup `bid` of a grid of one workgroup per tile owns: XCD-contiguous numbering, then groups of
 // kGroup row panels, so the ~32 workgroups resident on one XCD share operand steps
 // in its L2.
 template <int kGroup>
-__device__ __forceinline__ void gemm_tile(int tiles_m, int tiles_n, int& m0, int& n0) {
+__device__ __forceinline__ void gemm_tile(int tiles_m, int tiles_n, int bid, int& m0, int& n0) {
   const int G = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
   const int xcd = bid & 7, local = bid >> 3;
   const int q8 = G >> 3, r8 = G & 7;
   const int L = (xcd < r8) ? xcd * (q8 + 1) + local : r8 * (q8 + 1) + (xcd - r8) * q8 + local;
@@ -296,12 +295,20 @@ __device__ __forceinline__ void mfma_loop(Operand<kLA>& opa, Operand<kLB>& opb, 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// The thread index of a tile body passes through an empty asm, so that nothing derived
+// from it is hoisted out of the persistent tile loop and kept live across tiles.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 template <int kLA, int kLB>
-__global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int nk) {
+__device__ __forceinline__ void gemm_mfma_tile(const GemmArgs& g, int tiles_m, int tiles_n, int nk, int bid) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kGLds];
   int m0, n0;
-  gemm_tile<kGGroupM>(tiles_m, tiles_n, m0, n0);
-  const int tid = threadIdx.x, lane = tid & 63;
+  gemm_tile<kGGroupM>(tiles_m, tiles_n, bid, m0, n0);
+  const int tid = opaque_tid(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2, slot = wave & 3;
 
@@ -350,6 +357,18 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int
   }
 }
 
+// Persistent over tiles, as the single-launch prefill kernel: at most one workgroup per CU
+// (a multiple of 8) takes the tiles a grid of one workgroup per tile would start, in that
+// order; no workgroup waits for another.
+template <int kLA, int kLB>
+__global__ __launch_bounds__(kGThreads, 1) void gemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n, int nk) {
+  const int G = tiles_m * tiles_n;
+  for (int vb = blockIdx.x; vb < G; vb += (int)gridDim.x) {
+    gemm_mfma_tile<kLA, kLB>(g, tiles_m, tiles_n, nk, vb);
+    __syncthreads();  // the next tile's first steps overwrite the output staging
+  }
+}
+
 // ---- the pre-normalised QKV forward on the same loop (the opt-in pre-pass form): A is
 // the pre-pass's tiled bf16(x * w_norm) [T_pad, H], B the weight [H, N].  Wave (g, s)
 // holds rows 128 g .. +127 and two 32-column halves d/2 apart, so both members of every
@@ -365,13 +384,13 @@ __device__ __forceinline__ int pre_first_half(int s) {
 }
 
 template <int kD>
-__global__ __launch_bounds__(kGThreads, 1) void prefill_pre_kernel(ForwardArgs a, int tiles_m, int tiles_n, int nk) {
+__device__ __forceinline__ void prefill_pre_tile(const ForwardArgs& a, int tiles_m, int tiles_n, int nk, int bid) {
   // the rings, then (epilogue) 8 per-wave staging regions over them and the row information
   __shared__ __attribute__((aligned(16))) uint8_t smem[kGLds + 3 * GM * 4];
   static_assert(8 * 16384 <= kGLds, "staging regions inside the rings");
   int m0, n0;
-  gemm_tile<kGPreGroupM>(tiles_m, tiles_n, m0, n0);
-  const int tid = threadIdx.x, lane = tid & 63;
+  gemm_tile<kGPreGroupM>(tiles_m, tiles_n, bid, m0, n0);
+  const int tid = opaque_tid(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2, slot = wave & 3;
   const int H = a.H, N = a.N, T = a.T;
@@ -503,6 +522,15 @@ __global__ __launch_bounds__(kGThreads, 1) void prefill_pre_kernel(ForwardArgs a
   }
 }
 
+template <int kD>
+__global__ __launch_bounds__(kGThreads, 1) void prefill_pre_kernel(ForwardArgs a, int tiles_m, int tiles_n, int nk) {
+  const int G = tiles_m * tiles_n;
+  for (int vb = blockIdx.x; vb < G; vb += (int)gridDim.x) {
+    prefill_pre_tile<kD>(a, tiles_m, tiles_n, nk, vb);
+    __syncthreads();  // the next tile's first steps overwrite the output staging
+  }
+}
+
 // ---- plain FMA GEMM: 64 x 64 tile per 256-thread block, 4 x 4 results per thread,
 // K in chunks of 16 staged in LDS as fp32; results in the operands' dtype.
 template <bool BF16>
@@ -570,7 +598,8 @@ template <int kLA, int kLB>
 hipError_t run_mfma(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (g.M + GM - 1) / GM, tiles_n = (g.N + GN - 1) / GN;
   const int nk = ((g.K + GK - 1) / GK + 3) / 4 * 4;  // whole groups of 4 steps; the extra read zeros
-  gemm_mfma_kernel<kLA, kLB><<<dim3(tiles_m * tiles_n), dim3(kGThreads), 0, s>>>(g, tiles_m, tiles_n, nk);
+  gemm_mfma_kernel<kLA, kLB><<<dim3(persistent_grid(tiles_m * tiles_n)), dim3(kGThreads), 0, s>>>(g, tiles_m, tiles_n,
+                                                                                                  nk);
   return hipGetLastError();
 }
 
@@ -593,7 +622,7 @@ bool prefill_pre_supports(int H, int N, int d) {
 hipError_t launch_prefill_pre(const ForwardArgs& a, hipStream_t s) {
   if (!a.prenormed || !prefill_pre_supports(a.H, a.N, a.d)) return hipErrorInvalidValue;
   const int tiles_m = (a.T + GM - 1) / GM, tiles_n = a.N / GN, nk = a.H / GK;
-  const dim3 grid(tiles_m * tiles_n), block(kGThreads);
+  const dim3 grid(persistent_grid(tiles_m * tiles_n)), block(kGThreads);
   if (a.d == 64)
     prefill_pre_kernel<64><<<grid, block, 0, s>>>(a, tiles_m, tiles_n, nk);
   else if (a.d == 256)

@@ -55,6 +55,12 @@ bool prefill_supports(int H, int N, int Nq, int Nkv, int d);
 // multiple of 512 and H of 128.
 hipError_t launch_prefill_wide(const ForwardArgs& a, hipStream_t stream);
 bool prefill_wide_supports(int H, int N, int Nq, int Nkv, int d);
+// Workgroups of a tile-persistent launch over `tiles` tiles on the current device: one
+// per CU (the CU count rounded down to a multiple of 8, so that a workgroup's XCD is the
+// same for every tile it takes), or `tiles` if that is fewer.  The CU count is looked up
+// once per device (an attribute query, no stream work, so a forward under graph capture
+// may run it); should the query fail, every tile gets a workgroup of its own.
+int persistent_grid(int tiles);
 // The split-K form of the prefill kernel (two K slices per 256 x 256 tile, partial
 // tiles added by the last-arriving workgroup) is used up to this many tiles, one arrival
 // counter each.

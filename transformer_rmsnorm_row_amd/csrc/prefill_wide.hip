@@ -581,25 +581,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_wide_kernel(ForwardArgs a
   }
 }
 
-// Workgroups of a launch over G tiles on the current device: one per CU (rounded down to
-// a multiple of 8), or G if that is fewer.  The CU count is looked up once per device (a
-// device attribute query, no stream work, so a forward under graph capture may run it);
-// should the query fail, every tile gets a workgroup of its own, which is also correct.
-int wide_grid(int G) {
+
+}  // namespace
+
+int persistent_grid(int tiles) {
   static std::atomic<int> cus[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return G;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return tiles;
   int c = cus[dev].load(std::memory_order_relaxed);
   if (c == 0) {
     int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) return G;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) return tiles;
     c = n - n % 8;
     cus[dev].store(c, std::memory_order_relaxed);
   }
-  return G < c ? G : c;
+  return tiles < c ? tiles : c;
 }
-
-}  // namespace
 
 bool prefill_wide_supports(int H, int N, int Nq, int Nkv, int d) {
   return (d == 64 || d == 128 || d == 256) && H % (4 * WK) == 0 && N % WN == 0 && Nq % 128 == 0 &&
@@ -612,13 +609,13 @@ hipError_t launch_swiglu_wide(const ForwardArgs& a, hipStream_t stream) {
   // a.N = 2I columns of [gate | up]; the output (a.q) is [T, I]
   if (!swiglu_wide_supports(a.H, a.N / 2)) return hipErrorInvalidValue;
   const int tiles_m = (a.T + WM - 1) / WM, tiles_n = a.N / WN;
-  prefill_wide_kernel<128, true><<<dim3(wide_grid(tiles_m * tiles_n)), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
+  prefill_wide_kernel<128, true><<<dim3(persistent_grid(tiles_m * tiles_n)), dim3(kThreads), 0, stream>>>(a, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_wide(const ForwardArgs& a, hipStream_t stream) {
   const int tiles_m = (a.T + WM - 1) / WM, tiles_n = a.N / WN;
-  const dim3 grid(wide_grid(tiles_m * tiles_n)), block(kThreads);
+  const dim3 grid(persistent_grid(tiles_m * tiles_n)), block(kThreads);
   if (a.d == 64)
     prefill_wide_kernel<64><<<grid, block, 0, stream>>>(a, tiles_m, tiles_n);
   else if (a.d == 256)
