@@ -74,8 +74,9 @@ def test_prefill_full_size_sampled_rows(cid, prepass):
 def test_prefill_largest_plan():
     """The largest token count a plan of the Llama-3-8B GQA shape accepts: kernels use
     32-bit byte offsets, so tokens x widest row (6144 columns) x 2 bytes stays below
-    2^31.  One forward over 174761 tokens (682 full 256-row tiles and a ragged one,
-    16392 workgroups), sampled rows against the oracle; one token more is refused."""
+    2^31.  One forward over 174761 tokens (1365 full 128-row panels and a ragged one:
+    16392 tiles of 128 x 512, 64 rounds of the persistent grid and a partial one),
+    sampled rows against the oracle; one token more is refused."""
     base = workloads.WORKLOADS[3]
     limit = (1 << 31) // (base.n_total * 2)
     wl = base.with_tokens(1, limit - 1)
