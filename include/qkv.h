@@ -249,15 +249,19 @@ qkv_status qkv_forward_unfused(qkv_plan plan, int64_t num_tokens,
  * dx_j = r w_j ga_j - (r^3/H) x_j sum_k ga_k w_k x_k.  The page
  * "Liger-Kernel核心技术：RollingBuffer与融合算子详解" reports backward speed-ups for its
  * fused kernels next to the forward ones (section "算子融合").
+ * The normalised activations are never formed: r scales the unrotated gradient
+ * (g = r gy, rounded once to the plan dtype), so that dW = diag(w) x^T g with x itself
+ * as the GEMM operand, G = g W^T = r ga, db = sum_t g / r, dw_norm = sum_t G x and
+ * dx_j = w_j G_j - (r^2/H) x_j sum_k G_k w_k x_k -- the same algebra.
  * Every step, the two products included, runs on this library's kernels: for bf16
- * plans both GEMMs on the matrix cores (bf16 operands, fp32 accumulation; ga = gy W^T
+ * plans both GEMMs on the matrix cores (bf16 operands, fp32 accumulation; G = g W^T
  * there when N is a multiple of 32, else on fp32 FMA tiles), for fp32 plans on fp32
- * FMA tiles.  dW and the intermediate ga are rounded once to the plan dtype from their
- * fp32 sums.
+ * FMA tiles.  dW and the intermediate G are rounded once to the plan dtype from their
+ * fp32 results.
  * Column sums are done in a fixed order and every GEMM element is one fixed-order
  * sum, so results are deterministic.
  * Scratch: the first backward call through a plan allocates the plan's backward
- * scratch (about max_tokens * (N + 2H) * e + 8192 H bytes, e = element size), kept until
+ * scratch (about max_tokens * (N + H) * e + 8192 H bytes, e = element size), kept until
  * qkv_plan_destroy; later calls allocate nothing.  Forwards and backwards through one
  * plan share scratch and must not overlap in time.
  * Limits: ceil(num_tokens / 32) * 32 * N * e < 2^31 (the transposed upstream gradient

@@ -2,10 +2,10 @@
 
 Bar, derived from the arithmetic: every gradient element is a sum of many terms (over
 tokens for dw_norm, dW and db; over output columns for dx) whose inputs are rounded
-once -- for bf16 plans the recomputed activations and the unrotated gradient go into
-the fp32-accumulating GEMMs as bf16, and the activation gradient they give is rounded
-once to bf16 before the norm gradient -- so its error is relative to the root-sum-square
-s of those terms, not to the sum itself, which can cancel.  The test requires
+once -- for bf16 plans the unrotated gradient scaled by each token's r goes into the
+fp32-accumulating GEMMs as bf16 (next to x itself), and the activation gradient they
+give is rounded once to bf16 before the norm gradient -- so its error is relative to
+the root-sum-square s of those terms, not to the sum itself, which can cancel.  The test requires
 |gpu - oracle| <= tol * (1 + |oracle| + s) elementwise, tol = 1e-4 for fp32 plans and
 2e-2 for bf16 plans (s from the oracle), and reports the plain (1 + |oracle|) ratio
 too.  NaN/Inf fails.

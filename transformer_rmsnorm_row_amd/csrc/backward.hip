@@ -1,24 +1,32 @@
 // Backward of the fused attention-input chain: the elementwise and row/column
-// reduction kernels around the two plain GEMMs (which rocBLAS runs, see qkv_api.hip).
+// reduction kernels around the two plain GEMMs (gemm.hip).
 //
 // Chain rule of the forward (RMSNorm -> projection (+bias) -> rotate-half rotary
 // embedding of Q and K) for upstream gradients dQ, dK, dV, with r[t] the token's
 // inverse RMS and a = x r w the normalised activations:
-//   gy   = the rotation by -angle of each (dQ, dK) pair, dV unchanged   (unrotate)
-//   db   = sum over tokens of gy                                        (column sum)
-//   dW   = a^T gy,  ga = gy W^T                                         (GEMMs; ga rounded
-//                                                                         once to the plan dtype)
-//   dw   = sum over tokens of ga * x * r                                (column sum)
-//   dx_j = r w_j ga_j - (r^3 / H) x_j sum_k ga_k w_k x_k                (row kernel)
-// gy is stored transposed, gy^T [N][Tp] with Tp = T rounded up to 32 and the pad zero:
-// both GEMMs then take one operand with k contiguous and one with k as the row index,
-// the pairing the MFMA GEMM runs fastest.  Column sums are two-pass (fixed chunks of
-// tokens, then the chunks in order) and row sums one wave per row in a fixed order, so
-// every result is deterministic.
+//   gy   = the rotation by -angle of each (dQ, dK) pair, dV unchanged
+//   db   = sum over tokens of gy
+//   dW   = a^T gy,  ga = gy W^T
+//   dw   = sum over tokens of ga * x * r
+//   dx_j = r w_j ga_j - (r^3 / H) x_j sum_k ga_k w_k x_k
+// Both r and w are folded out of the normalised activations, which are never formed:
+// with g = r gy (each token's row scaled by its r, rounded once to the plan dtype) and
+// G = g W^T = r ga,
+//   dW   = diag(w) x^T g          (x itself is the GEMM operand; w scales the result rows)
+//   db   = sum over tokens of g / r
+//   dw   = sum over tokens of G * x
+//   dx_j = w_j G_j - (r^2 / H) x_j sum_k G_k w_k x_k
+// which is the same algebra (the page's operator-fusion section fuses the norm into the
+// projection the same way).  g is stored transposed, g^T [N][Tp] with Tp = T rounded up
+// to 32 and the pad zero: both GEMMs then take one operand with k contiguous and one with
+// k as the row index, the pairing the MFMA GEMM runs fastest.  Column sums are two-pass
+// (fixed chunks of tokens, then the chunks in order) and row sums one wave per row in a
+// fixed order, so every result is deterministic.
 #include <algorithm>
 
 #include "device_common.h"
 #include "backward.h"
+#include "launch.h"
 
 namespace qkv {
 
@@ -76,10 +84,10 @@ __device__ __forceinline__ void st8(void* p, size_t i, const float (&v)[8]) {
   }
 }
 
-// Unrotate and transpose: block (64 tokens, 32 consecutive rotation pairs) reads the
-// pairs' two columns from dq, dk or dv (Q and K pairs turned back by -angle, V pairs
-// copied), stages them in LDS as [64 columns][64 tokens], and writes the 64 gy^T rows'
-// 64-token pieces.  Pairs enumerate features i < d/2 of every head of Q, K and V; pair u
+// Unrotate, scale and transpose: block (64 tokens, 32 consecutive rotation pairs) reads
+// the pairs' two columns from dq, dk or dv (Q and K pairs turned back by -angle, V pairs
+// copied), multiplies them by the token's r, stages them in LDS as [64 columns][64
+// tokens], and writes the 64 g^T rows' 64-token pieces.  Pairs enumerate features i < d/2 of every head of Q, K and V; pair u
 // is column (u / half) d + u % half and its partner is half further.  Tokens in [T, Tp)
 // are written as zeros.
 template <bool BF16>
@@ -110,6 +118,9 @@ __global__ __launch_bounds__(256) void unrotate_t_kernel(BackwardArgs b, int tp)
         y0 = gu * cs + gv * sn;
         y1 = gv * cs - gu * sn;
       }
+      const float r = b.inv_rms[tt];
+      y0 *= r;
+      y1 *= r;
     }
     s[j][t] = y0;
     s[32 + j][t] = y1;
@@ -161,6 +172,12 @@ __global__ __launch_bounds__(256) void unrotate_t8_kernel(BackwardArgs b, int tp
           gv[k] = x1 * cs - x0 * sn;
         }
       }
+      const float r = b.inv_rms[tt];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        gu[k] *= r;
+        gv[k] *= r;
+      }
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -181,75 +198,29 @@ __global__ __launch_bounds__(256) void unrotate_t8_kernel(BackwardArgs b, int tp
   }
 }
 
-// db[n] = sum over tokens of gy^T[n][t]: one wave per row, lane partial sums over
-// 8-token pieces in order, then a fixed shuffle tree.
+// db[n] = sum over tokens of g^T[n][t] / r[t]: one wave per row, lane partial sums over
+// 8-token pieces in order, then a fixed shuffle tree.  Tokens of the zero pad (t >= T)
+// add nothing.
 template <bool BF16>
 __global__ __launch_bounds__(256) void rowsum_kernel(BackwardArgs b, int tp) {
   const int lane = threadIdx.x & 63;
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= b.N) return;
   float acc = 0.f;
-  for (int t = lane * 8; t < tp; t += 512) {
+  for (int t = lane * 8; t < b.T; t += 512) {
     float v[8];
     ld8<BF16>(b.gy, (size_t)n * tp + t, v);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc += v[j];
+    for (int j = 0; j < 8; ++j)
+      if (t + j < b.T) acc += v[j] / b.inv_rms[t + j];
   }
   acc = wave_sum(acc);
   if (lane == 0) st<BF16>(b.dbias, n, acc);
 }
 
-// One wave per token: r[t] and the normalised activations a = x r w in the plan dtype.
-// KIT > 0: H = 512 KIT, and the lane's KIT x 8 values of the row stay in registers
-// between the two passes (same arithmetic, same order); KIT = 0: any H, row read twice.
-template <bool BF16, int KIT>
-__global__ __launch_bounds__(256) void activations_kernel(BackwardArgs b) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= b.T) return;
-  const size_t row = (size_t)t * b.H;
-  if constexpr (KIT > 0) {
-    float v[KIT][8];
-    float ss = 0.f;
-#pragma unroll
-    for (int m = 0; m < KIT; ++m) {
-      ld8<BF16>(b.x, row + lane * 8 + 512 * m, v[m]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ss = fmaf(v[m][j], v[m][j], ss);
-    }
-    const float r = rsqrtf(wave_sum(ss) / (float)b.H + b.eps);
-    if (lane == 0) b.inv_rms[t] = r;
-#pragma unroll
-    for (int m = 0; m < KIT; ++m) {
-      float w[8];
-      ld8<BF16>(b.w_norm, lane * 8 + 512 * m, w);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[m][j] = v[m][j] * r * w[j];
-      st8<BF16>(b.act, row + lane * 8 + 512 * m, v[m]);
-    }
-    return;
-  }
-  float ss = 0.f;
-  for (int k = lane * 8; k < b.H; k += 512) {
-    float v[8];
-    ld8<BF16>(b.x, row + k, v);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
-  }
-  const float r = rsqrtf(wave_sum(ss) / (float)b.H + b.eps);
-  if (lane == 0) b.inv_rms[t] = r;
-  for (int k = lane * 8; k < b.H; k += 512) {
-    float v[8], w[8];
-    ld8<BF16>(b.x, row + k, v);
-    ld8<BF16>(b.w_norm, k, w);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = v[j] * r * w[j];
-    st8<BF16>(b.act, row + k, v);
-  }
-}
-
-// One wave per token: dx from ga (fp32), x, w and r.  KIT as for the activations:
-// the lane's ga and x values stay in registers between the inner product and dx.
+// One wave per token: dx from G = r ga, x, w and r.  KIT > 0: H = 512 KIT, and the
+// lane's KIT x 8 values of G and x stay in registers between the inner product and dx;
+// KIT = 0: any H, rows read twice.
 template <bool BF16, int KIT>
 __global__ __launch_bounds__(256) void norm_grad_kernel(BackwardArgs b) {
   const int lane = threadIdx.x & 63;
@@ -270,13 +241,13 @@ __global__ __launch_bounds__(256) void norm_grad_kernel(BackwardArgs b) {
     }
     inner = wave_sum(inner);
     const float r = b.inv_rms[t];
-    const float c2 = r * r * r / (float)b.H * inner;
+    const float c2 = r * r / (float)b.H * inner;
 #pragma unroll
     for (int m = 0; m < KIT; ++m) {
       float w[8];
       ld8<BF16>(b.w_norm, lane * 8 + 512 * m, w);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) g[m][j] = r * w[j] * g[m][j] - c2 * x[m][j];
+      for (int j = 0; j < 8; ++j) g[m][j] = w[j] * g[m][j] - c2 * x[m][j];
       st8<BF16>(b.dx, row + lane * 8 + 512 * m, g[m]);
     }
     return;
@@ -292,21 +263,21 @@ __global__ __launch_bounds__(256) void norm_grad_kernel(BackwardArgs b) {
   }
   inner = wave_sum(inner);
   const float r = b.inv_rms[t];
-  const float c2 = r * r * r / (float)b.H * inner;
+  const float c2 = r * r / (float)b.H * inner;
   for (int k = lane * 8; k < b.H; k += 512) {
     float g[8], w[8], x[8];
     ld8<BF16>(b.ga, row + k, g);
     ld8<BF16>(b.w_norm, k, w);
     ld8<BF16>(b.x, row + k, x);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) g[j] = r * w[j] * g[j] - c2 * x[j];
+    for (int j = 0; j < 8; ++j) g[j] = w[j] * g[j] - c2 * x[j];
     st8<BF16>(b.dx, row + k, g);
   }
 }
 
 // dx as norm_grad_kernel, fused with the norm-weight gradient's column sums: each wave
 // takes `tpw` consecutive tokens in order, keeps its lane's KIT x 8 column sums of
-// ga x r in registers across them, and writes them as one row of `partial` (rows in
+// G x in registers across them, and writes them as one row of `partial` (rows in
 // wave order; the final pass adds them in that order).
 template <bool BF16, int KIT>
 __global__ __launch_bounds__(256) void norm_grad_fused_kernel(BackwardArgs b, int tpw, int nparts) {
@@ -335,15 +306,15 @@ __global__ __launch_bounds__(256) void norm_grad_fused_kernel(BackwardArgs b, in
     }
     inner = wave_sum(inner);
     const float r = b.inv_rms[t];
-    const float c2 = r * r * r / (float)b.H * inner;
+    const float c2 = r * r / (float)b.H * inner;
 #pragma unroll
     for (int m = 0; m < KIT; ++m) {
       float w[8], d[8];
       ld8<BF16>(b.w_norm, lane * 8 + 512 * m, w);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        d[j] = r * w[j] * g[m][j] - c2 * x[m][j];
-        col[m][j] = fmaf(g[m][j] * x[m][j], r, col[m][j]);
+        d[j] = w[j] * g[m][j] - c2 * x[m][j];
+        col[m][j] = fmaf(g[m][j], x[m][j], col[m][j]);
       }
       st8<BF16>(b.dx, row + lane * 8 + 512 * m, d);
     }
@@ -353,7 +324,7 @@ __global__ __launch_bounds__(256) void norm_grad_fused_kernel(BackwardArgs b, in
 }
 
 // Column sums over tokens, pass 1: block (column group, token chunk) -> fp32 partial
-// of ga[t, c] * x[t, c] * r[t].
+// of G[t, c] * x[t, c].
 template <bool BF16>
 __global__ __launch_bounds__(256) void colsum_partial_kernel(BackwardArgs b, int ncols, int chunks) {
   const int c = blockIdx.x * 256 + threadIdx.x;
@@ -364,7 +335,7 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(BackwardArgs b, int
   // unrolled so that the loads of several tokens are in flight; the adds keep token order
 #pragma unroll 8
   for (int t = t0; t < t1; ++t) {
-    s = fmaf(ld<BF16>(b.ga, (size_t)t * ncols + c) * ld<BF16>(b.x, (size_t)t * ncols + c), b.inv_rms[t], s);
+    s = fmaf(ld<BF16>(b.ga, (size_t)t * ncols + c), ld<BF16>(b.x, (size_t)t * ncols + c), s);
   }
   b.partial[(size_t)blockIdx.y * ncols + c] = s;
 }
@@ -417,17 +388,13 @@ hipError_t colsum(const BackwardArgs& b, int ncols, void* out, hipStream_t strea
 template <bool BF16>
 hipError_t pre_gemm(const BackwardArgs& b, hipStream_t stream) {
   const int tp = backward_token_pitch(b.T);
+  // r first: the unrotate kernel scales by it
+  const hipError_t e = launch_inv_rms(b.x, b.inv_rms, b.T, b.H, b.eps, BF16, stream);
+  if (e != hipSuccess) return e;
   if ((b.d / 2) % 8 == 0)
     unrotate_t8_kernel<BF16><<<dim3((tp + 63) / 64, (b.N / 2 + 63) / 64), dim3(256), 0, stream>>>(b, tp);
   else
     unrotate_t_kernel<BF16><<<dim3((tp + 63) / 64, (b.N / 2 + 31) / 32), dim3(256), 0, stream>>>(b, tp);
-  const dim3 rows((b.T + 3) / 4), threads(256);
-  switch (b.H) {
-    case 1024: activations_kernel<BF16, 2><<<rows, threads, 0, stream>>>(b); break;
-    case 2048: activations_kernel<BF16, 4><<<rows, threads, 0, stream>>>(b); break;
-    case 4096: activations_kernel<BF16, 8><<<rows, threads, 0, stream>>>(b); break;
-    default: activations_kernel<BF16, 0><<<rows, threads, 0, stream>>>(b); break;
-  }
   if (b.dbias) rowsum_kernel<BF16><<<dim3((b.N + 3) / 4), dim3(256), 0, stream>>>(b, tp);
   return hipGetLastError();
 }

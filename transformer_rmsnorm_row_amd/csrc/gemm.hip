@@ -332,6 +332,23 @@ __device__ __forceinline__ void gemm_mfma_tile(const GemmArgs& g, int tiles_m, i
   uint8_t* ws = smem + wave * 16384;
   const uint32_t swz = ((uint32_t)lane >> 4) << 4;  // 16 ((row >> 2) & 3) of every row this lane writes
   const auto c_rsrc = make_rsrc(g.c, (uint32_t)g.M * (uint32_t)g.ldc * 2u);
+  // row scales of the lane's 32 rows (1 without row_scale; rows past M read 0)
+  float rsc[8][4];
+  if (g.row_scale) {
+    const auto s_rsrc = make_rsrc(g.row_scale, (uint32_t)g.M * 2u);
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t grow = (uint32_t)(m0 + 128 * grp) + 16u * rb + 4u * ((uint32_t)lane >> 4) + i;
+        rsc[rb][i] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(s_rsrc, (int)(grow * 2u), 0, 0));
+      }
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rsc[rb][i] = 1.f;
+  }
 #pragma unroll
   for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
@@ -341,8 +358,8 @@ __device__ __forceinline__ void gemm_mfma_tile(const GemmArgs& g, int tiles_m, i
         const uint32_t row = 16u * rb + 4u * ((uint32_t)lane >> 4) + i;
         const uint32_t col = (16u * cb + ((uint32_t)lane & 15u)) ^ swz;
         // the element is copied out as a float first (a bit cast taken straight from a
-        // vector element has been miscompiled)
-        const float v = acc[rb][cb][i];
+        // vector element has been miscompiled); then scaled in fp32 and rounded once
+        const float v = acc[rb][cb][i] * rsc[rb][i];
         *reinterpret_cast<uint16_t*>(ws + row * 128u + col * 2u) = f32_to_bf16(v);
       }
 #pragma unroll
@@ -585,11 +602,12 @@ __global__ __launch_bounds__(256) void gemm_fma_kernel(GemmArgs g) {
     for (int j = 0; j < 4; ++j) {
       const int m = m0 + tm + 16 * i, n = n0 + tn + 16 * j;
       if (m < g.M && n < g.N) {
+        const float v = g.row_scale ? acc[i][j] * gload<BF16>(g.row_scale, m) : acc[i][j];
         // the operands' dtype, rounded once for bf16
         if constexpr (BF16)
-          ((uint16_t*)g.c)[(size_t)m * g.ldc + n] = f32_to_bf16(acc[i][j]);
+          ((uint16_t*)g.c)[(size_t)m * g.ldc + n] = f32_to_bf16(v);
         else
-          ((float*)g.c)[(size_t)m * g.ldc + n] = acc[i][j];
+          ((float*)g.c)[(size_t)m * g.ldc + n] = v;
       }
     }
 }
@@ -634,21 +652,22 @@ hipError_t launch_prefill_pre(const ForwardArgs& a, hipStream_t s) {
 
 hipError_t launch_backward_gemms(const BackwardArgs& b, void* dw, hipStream_t s) {
   const int tp = backward_token_pitch(b.T);
-  // dW [H, N] (plan dtype) = a^T gy: M = H, N = N, K = T; a [T, H] is [K][cols] and its
-  // buffer range ends at row T (the last step's rows past it read zeros), gy^T [N, Tp] is
-  // [rows][K] with a zero pad from T to Tp (the last step reads it in whole 32-wide k
-  // pieces)
+  // dW [H, N] (plan dtype) = diag(w_norm) x^T g: M = H, N = N, K = T; x [T, H] is
+  // [K][cols] and its buffer range ends at row T (the last step's rows past it read
+  // zeros), g^T [N, Tp] is [rows][K] with a zero pad from T to Tp (the last step reads it
+  // in whole 32-wide k pieces); w_norm scales the result rows
   GemmArgs w{};
-  w.a = b.act;
+  w.a = b.x;
   w.b = b.gy;
   w.c = dw;
+  w.row_scale = b.w_norm;
   w.M = b.H;
   w.N = b.N;
   w.K = b.T;
   w.lda = b.H;
   w.ldb = tp;
   w.ldc = b.N;
-  // ga [T, H] (plan dtype) = gy W^T: M = T, N = H, K = N; gy^T [N, Tp] is [K][cols], W
+  // G [T, H] (plan dtype) = g W^T: M = T, N = H, K = N; g^T [N, Tp] is [K][cols], W
   // [H, N] is [rows][K]
   GemmArgs a{};
   a.a = b.gy;

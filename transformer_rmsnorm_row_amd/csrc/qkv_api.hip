@@ -43,7 +43,6 @@ struct Plan {
   void* xw;           // QKV_PLAN_PREFILL_PREPASS: bf16(x * w_norm) from the pre-pass, max_tokens rounded up to 256 rows
   // backward scratch, allocated by the first qkv_backward through the plan
   void* bwd_gy;         // [max_tokens, N] plan dtype
-  void* bwd_act;        // [max_tokens, H] plan dtype
   void* bwd_ga;         // [max_tokens, H] plan dtype
   float* bwd_partial;   // [kBackwardPartials, H] fp32
   rocblas_handle blas;  // the unfused forward's GEMM (created on its first call)
@@ -108,7 +107,6 @@ void free_scratch(Plan* pl) {
   if (pl->kcount) (void)hipFree(pl->kcount);
   if (pl->xw) (void)hipFree(pl->xw);
   if (pl->bwd_gy) (void)hipFree(pl->bwd_gy);
-  if (pl->bwd_act) (void)hipFree(pl->bwd_act);
   if (pl->bwd_ga) (void)hipFree(pl->bwd_ga);
   if (pl->bwd_partial) (void)hipFree(pl->bwd_partial);
   if (pl->blas) (void)rocblas_destroy_handle(pl->blas);
@@ -119,7 +117,7 @@ void free_scratch(Plan* pl) {
   pl->kpart = nullptr;
   pl->xw = nullptr;
   pl->kcount = nullptr;
-  pl->bwd_gy = pl->bwd_act = nullptr;
+  pl->bwd_gy = nullptr;
   pl->bwd_ga = pl->bwd_partial = nullptr;
   pl->blas = nullptr;
 }
@@ -147,7 +145,6 @@ qkv_status ensure_backward_scratch(Plan* pl) {
   // each buffer is allocated once: a call after a failed allocation keeps what succeeded
   const size_t tp = (size_t)qkv::backward_token_pitch((int)T);
   bool ok = (pl->bwd_gy || hipMalloc(&pl->bwd_gy, tp * N * elem) == hipSuccess) &&
-            (pl->bwd_act || hipMalloc(&pl->bwd_act, T * H * elem) == hipSuccess) &&
             (pl->bwd_ga || hipMalloc(&pl->bwd_ga, T * H * elem) == hipSuccess) &&
             hipMalloc(&pl->bwd_partial, (size_t)qkv::kBackwardPartials * H * sizeof(float)) == hipSuccess;
   if (!ok) {
@@ -692,7 +689,6 @@ qkv_status qkv_backward(qkv_plan plan, int64_t num_tokens, const void* x, const 
   b.dw_norm = dw_norm;
   b.dbias = dbias;
   b.gy = pl->bwd_gy;
-  b.act = pl->bwd_act;
   b.ga = pl->bwd_ga;
   b.inv_rms = pl->inv_rms;
   b.partial = pl->bwd_partial;
@@ -707,7 +703,7 @@ qkv_status qkv_backward(qkv_plan plan, int64_t num_tokens, const void* x, const 
   b.bf16 = pl->bf16;
   if (qkv::launch_backward_pre_gemm(b, s) != hipSuccess) return QKV_ERR_HIP;
 
-  // dW = a^T gy straight into the caller's dw_qkv, ga = gy W^T into plan scratch
+  // dW = diag(w_norm) x^T g straight into the caller's dw_qkv, G = g W^T into plan scratch
   if (qkv::launch_backward_gemms(b, dw_qkv, s) != hipSuccess) return QKV_ERR_HIP;
   return qkv::launch_backward_post_gemm(b, s) == hipSuccess ? QKV_OK : QKV_ERR_HIP;
 }
