@@ -99,6 +99,7 @@ __global__ __launch_bounds__(256) void unrotate_t_kernel(BackwardArgs b, int tp)
     const int t = e >> 5, j = e & 31, u = u0 + j, tt = t0 + t;
     float y0 = 0.f, y1 = 0.f;
     if (u < npairs && tt < b.T) {
+      const float r = b.inv_rms[tt];  // requested first: its latency overlaps the gradient loads
       const int c = (u / half) * b.d + (u % half);
       const void* src;
       int width, oc;
@@ -118,7 +119,6 @@ __global__ __launch_bounds__(256) void unrotate_t_kernel(BackwardArgs b, int tp)
         y0 = gu * cs + gv * sn;
         y1 = gv * cs - gu * sn;
       }
-      const float r = b.inv_rms[tt];
       y0 *= r;
       y1 *= r;
     }
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void unrotate_t8_kernel(BackwardArgs b, int tp
 #pragma unroll
     for (int k = 0; k < 8; ++k) gu[k] = gv[k] = 0.f;
     if (u < npairs && tt < b.T) {
-      const int c = (u / half) * b.d + (u % half);
+      const int c = (u / half) * b.d + (u % half), i0 = u % half;
       const void* src;
       int width, oc;
       if (c < b.Nq) {
@@ -159,24 +159,24 @@ __global__ __launch_bounds__(256) void unrotate_t8_kernel(BackwardArgs b, int tp
       } else {
         src = b.dv; width = b.Nkv; oc = c - b.Nq - b.Nkv;
       }
+      // every load of the item is issued before any is used (one memory round trip): r,
+      // the position and frequencies (read for V pairs too, whose angles are unused), the
+      // two halves
+      const float r = b.inv_rms[tt];
+      const int32_t p = b.pos[tt];
+      double fr[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) fr[k] = b.rev_freq[i0 + k];
       ld8<BF16>(src, (size_t)tt * width + oc, gu);
       ld8<BF16>(src, (size_t)tt * width + oc + half, gv);
-      if (c < b.Nq + b.Nkv) {
-        const int i0 = u % half;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          float cs, sn;
-          rope_cos_sin(b.pos[tt], b.rev_freq[i0 + k], cs, sn);
-          const float x0 = gu[k], x1 = gv[k];
-          gu[k] = x0 * cs + x1 * sn;
-          gv[k] = x1 * cs - x0 * sn;
-        }
-      }
-      const float r = b.inv_rms[tt];
+      const bool rot = c < b.Nq + b.Nkv;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        gu[k] *= r;
-        gv[k] *= r;
+        float cs, sn;
+        rope_cos_sin(p, fr[k], cs, sn);
+        const float x0 = gu[k], x1 = gv[k];
+        gu[k] = (rot ? x0 * cs + x1 * sn : x0) * r;
+        gv[k] = (rot ? x1 * cs - x0 * sn : x1) * r;
       }
     }
 #pragma unroll
