@@ -312,6 +312,7 @@ qkv_status noalloc_scratch(int dev, uint8_t** out) {
       return QKV_ERR_HIP;
     }
     g_noalloc_ptr[dev] = static_cast<uint8_t*>(p);
+    (void)qkv::persistent_grid(1);  // the persistent kernels' CU count, once per device
   }
   *out = g_noalloc_ptr[dev];
   return QKV_OK;
@@ -343,6 +344,9 @@ qkv_status qkv_plan_create(const qkv_plan_desc* desc, qkv_plan* out_plan) {
     delete pl;
     return QKV_ERR_HIP;
   }
+  // the persistent kernels' CU count, looked up here once per device, outside any graph
+  // capture a later forward may run under
+  (void)qkv::persistent_grid(1);
   const int half = desc->head_dim / 2;
   bool ok = hipMalloc(&pl->inv_rms, sizeof(float) * (size_t)desc->max_tokens) == hipSuccess &&
             hipMalloc(&pl->rev_freq, sizeof(double) * (size_t)half) == hipSuccess;
