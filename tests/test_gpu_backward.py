@@ -76,6 +76,10 @@ CASES = {
                                                head_dim=64)),
     "fp32_d256": (workloads.WORKLOADS[1], dict(batch=1, seq=40, hidden=128, num_q_heads=2, num_kv_heads=1,
                                                 head_dim=256)),
+    # bf16 with N = 40 (not a multiple of 32): G = g W^T on the fp32-FMA tiles, and d = 8 takes
+    # the 2-byte unrotate kernel
+    "bf16_n40_d8": (workloads.WORKLOADS[3], dict(batch=1, seq=70, hidden=128, num_q_heads=3, num_kv_heads=1,
+                                                  head_dim=8)),
     # the shape the benchmark times the backward on: Llama-7B, 4 x 2048 tokens, every
     # element of every gradient against the oracle's full chain rule
     "llama7b_full": (workloads.WORKLOADS[2], {}),
