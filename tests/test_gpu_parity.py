@@ -163,6 +163,7 @@ PREPASS_CASES = [
     (3, 6000, {"hidden": 2048, "num_q_heads": 16, "num_kv_heads": 4, "head_dim": 64}),  # N = 1536
     (3, 3000, {"hidden": 512, "num_q_heads": 8, "num_kv_heads": 2, "head_dim": 256}),   # N = 3072
     (5, 777, {"hidden": 1024}),                                                         # MHA + bias
+    (2, 2500, {}),  # Llama-7B shape: 10 x 48 = 480 tiles, more than the persistent grid's workgroups
 ]
 
 
