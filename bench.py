@@ -296,8 +296,9 @@ def backward_leg(qkv, workloads, wl, bufs, steps: int = 10, warmup: int = 2):
     gemm_flops = 2 * wl.flops()
     return {"workload": wl.name, "us": round(sec * 1e6, 2), "gemm_flops": gemm_flops,
             "tflops": round(gemm_flops / sec / 1e12, 2), "mfma_frac": round(gemm_flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "note": "dW = a^T gy and ga = gy W^T on this library's 256 x 256 MFMA GEMM; unrotate, activations, "
-                    "norm gradient and column sums in its other kernels (no vendor library)"}
+            "note": "dW = diag(w) x^T g and G = g W^T (g = r gy) on this library's 256 x 256 MFMA GEMM; r, "
+                    "unrotate, norm gradient and column sums in its other kernels (no vendor library; the "
+                    "normalised activations are never formed)"}
 
 
 def _event_time(fn, steps: int, warmup: int) -> float:
