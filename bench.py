@@ -273,9 +273,9 @@ def decode_leg(qkv, workloads, replays: int = 125, copies: int = 8):
 
 
 def backward_leg(qkv, workloads, wl, bufs, steps: int = 10, warmup: int = 2):
-    """The backward of the chain on the workload's shape: unrotate, recomputed
-    activations, the two GEMMs (this library's MFMA kernel), norm gradient and column
-    sums."""
+    """The backward of the chain on the workload's shape: r, unrotate (scaled by r), the
+    two GEMMs (this library's MFMA kernel, x itself as dW's operand), norm gradient and
+    column sums."""
     import torch
     x, w, W, b, pos, q, k, v = bufs
     g = workloads.make_grads(wl)
