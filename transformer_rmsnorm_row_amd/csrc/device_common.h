@@ -31,6 +31,15 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
 __device__ __forceinline__ void buf_store16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, 0);
 }
+// The same as a non-temporal (streaming) store, for a forward's final outputs, which no
+// later step of the kernel reads: they do not displace the operand steps that the
+// workgroups of an XCD share in its L2 (measured on the single-launch prefill, two boxes:
+// Qwen-7B 1330-1333 -> 1307-1309 and 1323-1326 -> 1295-1302 us, the Llama-7B gated MLP
+// 1199-1200 -> 1182-1186 us, the pre-pass form's Qwen-7B pair 1169 -> 1159-1163 us; the
+// other prefill shapes unchanged).
+__device__ __forceinline__ void buf_store16_nt(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)byte_off, 0, 2);
+}
 
 // bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even and keeps
 // NaN a NaN (gfx950 v_cvt_pk_bf16_f32).

@@ -535,7 +535,7 @@ __device__ __forceinline__ void prefill_pre_tile(const ForwardArgs& a, int tiles
       orow = out_rows;  // past the buffer's range: dropped
     }
     const uint32_t col = ocol + (q < 4 ? 8u * q : (uint32_t)(kD / 2) + 8u * (q - 4));
-    buf_store16(v, ro, (orow * width + col) * 2u);
+    buf_store16_nt(v, ro, (orow * width + col) * 2u);
   }
 }
 

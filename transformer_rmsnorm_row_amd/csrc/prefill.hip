@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
       const uint32_t row = 64u * (slot & 1) + 8u * it + (lane >> 3);
       const u32x4 v = lds_read16(stage, row * kStagePitch + ch * 16u);
       const uint32_t grow = (uint32_t)(m0 + 128 * grp) + row;
-      buf_store16(v, ro, (grow * I + fcol + ch * 8u) * 2u);
+      buf_store16_nt(v, ro, (grow * I + fcol + ch * 8u) * 2u);
     }
   } else {
     // ---- epilogue: scale, bias, rotate, stage as bf16, store
@@ -666,7 +666,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(ForwardArgs a, int
         const int32_t sr = s_slot[128 * grp + row];
         orow = sr >= 0 && sr < a.cache_rows ? (uint32_t)sr : out_rows;
       }
-      buf_store16(v, ro, (orow * width + ocol + ch * 8u) * 2u);
+      buf_store16_nt(v, ro, (orow * width + ocol + ch * 8u) * 2u);
     }
   }
 }

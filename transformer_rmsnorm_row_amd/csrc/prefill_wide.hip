@@ -484,7 +484,7 @@ __device__ __forceinline__ void wide_tile(const ForwardArgs& a, int tiles_m, int
     for (int it = 0; it < 8; ++it) {
       const uint32_t row = 32u * (wave & 3) + 4u * it + (lane >> 4);
       const u32x4 v = lds_read16(stage, row * kStagePitch + ch * 16u);
-      buf_store16(v, ro, (((uint32_t)m0 + row) * I + fcol + ch * 8u) * 2u);
+      buf_store16_nt(v, ro, (((uint32_t)m0 + row) * I + fcol + ch * 8u) * 2u);
     }
   } else {
   // ---- epilogue: scale, bias, rotate, stage as bf16 per 128-column block, store
@@ -559,7 +559,7 @@ __device__ __forceinline__ void wide_tile(const ForwardArgs& a, int tiles_m, int
       const int32_t sr = s_slot[row];
       orow = sr >= 0 && sr < a.cache_rows ? (uint32_t)sr : out_rows;
     }
-    buf_store16(v, ro, (orow * width + ocol + ch * 8u) * 2u);
+    buf_store16_nt(v, ro, (orow * width + ocol + ch * 8u) * 2u);
   }
   }
 }
