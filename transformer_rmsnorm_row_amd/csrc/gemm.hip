@@ -370,7 +370,9 @@ __device__ __forceinline__ void gemm_mfma_tile(const GemmArgs& g, int tiles_m, i
     const int grow = m0 + 128 * grp + (int)row, gcol = n0 + 64 * slot + 8 * (int)q;
     // rows past M fall outside the buffer's range; columns past N are sent outside it
     const uint32_t off = gcol < g.N ? ((uint32_t)grow * (uint32_t)g.ldc + (uint32_t)gcol) * 2u : kOutside;
-    buf_store16(v, c_rsrc, off);
+    // non-temporal: measured on the Llama-7B backward (A/B, 6 calls each), 1451-1470 against
+    // 1458-1487 us
+    buf_store16_nt(v, c_rsrc, off);
   }
 }
 
